@@ -1,0 +1,272 @@
+// Stage 1 kernels: block pooling of Q/K/V and the OAM scoring GEMM.
+//
+// Source: "从Stem稀疏注意力看大模型推理的架构取舍", sections "OAM：价值评估" (score = routing relevance
+// QK^T + beta * log||V_j||_2) and "HPC-Stem：评估选块，快几十倍" (the additive score lets compact per-block
+// Q and K representations replace the token-level product, so all block scores come from one GEMM).
+//
+// pool_kernel   HBM-bound streaming reduction.  One workgroup owns one block (B tokens) and a 256-lane
+//               slice of the token row (16 bytes per lane per token, so every load is a coalesced 16-byte
+//               vector).  Q and K are summed in fp32 and divided by the number of valid tokens; V rows
+//               give ln||v||_2 per (token, head) through a shuffle reduction over the lanes of the head,
+//               averaged over the block.  Algorithmic bytes: one read of Q, K and V plus the fp32 outputs.
+// score_kernel  S = qbar kbar^T / sqrt(d) + beta M for the causal tile pairs of each request, fp32 FMA
+//               in a 64x64 register-blocked tile (4x4 per thread), d staged through LDS in chunks of 32.
+#include "stem_internal.h"
+
+namespace stem {
+
+namespace {
+
+constexpr int kPoolThreads = 256;
+
+// Decode one 16-byte vector into N = 16/EB floats.
+template <int EB>
+__device__ __forceinline__ void decode16(const uint4 w, float* x) {
+  if constexpr (EB == 4) {
+    x[0] = __uint_as_float(w.x);
+    x[1] = __uint_as_float(w.y);
+    x[2] = __uint_as_float(w.z);
+    x[3] = __uint_as_float(w.w);
+  } else if constexpr (EB == 2) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(u[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(u[i] >> 16);
+    }
+  } else {
+    fp8x4_to_f32(w.x, x);
+    fp8x4_to_f32(w.y, x + 4);
+    fp8x4_to_f32(w.z, x + 8);
+    fp8x4_to_f32(w.w, x + 12);
+  }
+}
+
+template <int EB>
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
+  constexpr int EPL = 16 / EB;  // elements per lane
+  const int ib = blockIdx.x;
+  int job = blockIdx.y;
+  int kind;  // 0 = Q mean, 1 = K mean, 2 = V log-norm mean
+  if (job < a.q_chunks) {
+    kind = 0;
+  } else if (job < a.q_chunks + a.kv_chunks) {
+    kind = 1;
+    job -= a.q_chunks;
+  } else {
+    kind = 2;
+    job -= a.q_chunks + a.kv_chunks;
+  }
+  const int H = kind == 0 ? a.hq : a.hkv;
+  const int d = a.d;
+  const int lpr = H * d / EPL;  // lanes per token row
+  const int chunk_lanes = min(lpr - job * kPoolThreads, kPoolThreads);
+  const int tr = kPoolThreads / chunk_lanes;  // token rows processed in parallel
+  const int tid = threadIdx.x;
+  const int rs = tid / chunk_lanes;
+  const int lic = tid % chunk_lanes;
+  const bool active = rs < tr;
+
+  const int r = find_request(a.rt, ib);
+  const int i = ib - a.rt.cu_blocks[r];
+  const int tb = a.rt.cu_seqlens[r];
+  const int L = a.rt.cu_seqlens[r + 1] - tb;
+  const int t0 = i * a.B;
+  const int t1 = min(t0 + a.B, L);
+  const int e0 = (job * kPoolThreads + lic) * EPL;  // first element of this lane in the token row
+  const int head = e0 / d;
+  const int dd = e0 % d;
+  const int hl = d / EPL;  // lanes per head
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float lacc = 0.f;
+
+  const uint8_t* base;
+  float vscale = 1.f;
+  if (kind == 0) {
+    base = (const uint8_t*)a.q;
+  } else {
+    base = (const uint8_t*)(kind == 1 ? a.k : a.v);
+    if (EB == 1 && kind == 2) vscale = a.v_scale[head];
+  }
+
+  auto row_ptr = [&](int t) -> const uint4* {
+    int64_t off;
+    if (kind == 0) off = (int64_t)(tb + t) * a.hq * d + e0;
+    else off = a.kv.row(r, tb, t, head) + dd;
+    return (const uint4*)(base + off * EB);
+  };
+
+  if (active) {
+    if (kind != 2) {
+      int t = t0 + rs;
+      for (; t + 3 * tr < t1; t += 4 * tr) {
+        uint4 w0 = *row_ptr(t), w1 = *row_ptr(t + tr), w2 = *row_ptr(t + 2 * tr), w3 = *row_ptr(t + 3 * tr);
+        float x[EPL];
+        decode16<EB>(w0, x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+        decode16<EB>(w1, x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+        decode16<EB>(w2, x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+        decode16<EB>(w3, x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+      }
+      for (; t < t1; t += tr) {
+        float x[EPL];
+        decode16<EB>(*row_ptr(t), x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+      }
+    }
+  }
+  if (kind == 2) {
+    // All lanes of a head must take part in the shuffle: iterate a uniform trip count per row slot.
+    for (int t = t0 + rs; t < t0 + a.B; t += tr) {
+      float ss = 0.f;
+      if (active && t < t1) {
+        float x[EPL];
+        decode16<EB>(*row_ptr(t), x);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float y = x[e] * vscale;
+          ss = fmaf(y, y, ss);
+        }
+      }
+      for (int m = 1; m < hl; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      if (active && t < t1) lacc += 0.5f * logf(ss);
+    }
+  }
+
+  // Combine the parallel token rows through LDS.
+  __shared__ float red[kPoolThreads * 16];
+  const int cnt = t1 - t0;
+  if (tr > 1) {
+    if (kind != 2) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[tid * EPL + e] = acc[e];
+    } else {
+      red[tid] = lacc;
+    }
+    __syncthreads();
+    if (rs == 0) {
+      for (int s = 1; s < tr; ++s) {
+        const int src = s * chunk_lanes + lic;
+        if (kind != 2) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += red[src * EPL + e];
+        } else {
+          lacc += red[src];
+        }
+      }
+    }
+  }
+  if (rs != 0) return;
+
+  const float inv = 1.f / (float)cnt;
+  if (kind == 2) {
+    if (lic % hl == 0) a.M[(int64_t)head * a.NB + ib] = lacc * inv;
+    return;
+  }
+  float sc = inv;
+  if constexpr (EB == 1) sc *= (kind == 0 ? a.q_scale[head] : a.k_scale[head]);
+  float* dst = (kind == 0 ? a.qbar : a.kbar) + ((int64_t)head * a.NB + ib) * d + dd;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) {
+    float4 o = make_float4(acc[e] * sc, acc[e + 1] * sc, acc[e + 2] * sc, acc[e + 3] * sc);
+    *(float4*)(dst + e) = o;
+  }
+}
+
+constexpr int kTile = 64;
+constexpr int kDChunk = 32;
+
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  const int r = blockIdx.z;
+  const int h = blockIdx.y;
+  const int pidx = blockIdx.x;
+  const int n = a.rt.cu_blocks[r + 1] - a.rt.cu_blocks[r];
+  const int nt = (n + kTile - 1) / kTile;
+  if (pidx >= nt * (nt + 1) / 2) return;
+  // tile pair (I, J), J <= I, from the linear index
+  int I = (int)((sqrtf(8.f * pidx + 1.f) - 1.f) * 0.5f);
+  while ((I + 1) * (I + 2) / 2 <= pidx) ++I;
+  while (I * (I + 1) / 2 > pidx) --I;
+  const int J = pidx - I * (I + 1) / 2;
+  const int g = h / (a.hq / a.hkv);
+  const int64_t cb = a.rt.cu_blocks[r];
+  const int d = a.d;
+
+  __shared__ float qs[kTile][kDChunk + 1];
+  __shared__ float ks[kTile][kDChunk + 1];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  float acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
+
+  const float* qb = a.qbar + ((int64_t)h * a.NB + cb) * d;
+  const float* kb = a.kbar + ((int64_t)g * a.NB + cb) * d;
+  for (int d0 = 0; d0 < d; d0 += kDChunk) {
+    // 64 rows x 32 floats per operand: 2048 floats, 8 per thread
+    for (int e = tid; e < kTile * kDChunk; e += 256) {
+      const int row = e / kDChunk, col = e % kDChunk;
+      const int qi = I * kTile + row, kj = J * kTile + row;
+      qs[row][col] = qi < n ? qb[(int64_t)qi * d + d0 + col] : 0.f;
+      ks[row][col] = kj < n ? kb[(int64_t)kj * d + d0 + col] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < kDChunk; ++c) {
+      float qa[4], kb4[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qa[x] = qs[ty + 16 * x][c];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) kb4[y] = ks[tx + 16 * y][c];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(qa[x], kb4[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+  const float* Mg = a.M + (int64_t)g * a.NB + cb;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int i = I * kTile + ty + 16 * x;
+    if (i >= n) continue;
+    float* row = a.scores + ((int64_t)h * a.NB + cb + i) * a.stride;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int j = J * kTile + tx + 16 * y;
+      if (j <= i) row[j] = fmaf(acc[x][y], a.inv_sqrt_d, a.beta * Mg[j]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s) {
+  dim3 grid((unsigned)a.NB, (unsigned)(a.q_chunks + 2 * a.kv_chunks));
+  if (dtype == STEM_F32) hipLaunchKernelGGL(pool_kernel<4>, grid, dim3(kPoolThreads), 0, s, a);
+  else if (dtype == STEM_BF16) hipLaunchKernelGGL(pool_kernel<2>, grid, dim3(kPoolThreads), 0, s, a);
+  else hipLaunchKernelGGL(pool_kernel<1>, grid, dim3(kPoolThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, int max_n, int num_reqs, hipStream_t s) {
+  const int nt = (max_n + kTile - 1) / kTile;
+  dim3 grid((unsigned)(nt * (nt + 1) / 2), (unsigned)a.hq, (unsigned)num_reqs);
+  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace stem

@@ -1,0 +1,137 @@
+// Stage 2 kernel: Token Position Decay budget fused with top-k block selection.
+//
+// Source: "从Stem稀疏注意力看大模型推理的架构取舍", sections "TPD：优先级排序" (linear decay of the per-position
+// top-k budget from k_start to k_end = mu k_start, same total as a uniform budget) and "HPC-Stem：评估选块，
+// 快几十倍" (budget generation is one formula per position and is fused with the selection sort, so no
+// budget tensor goes through HBM).
+//
+// One wavefront handles kRowsPerWave consecutive query-block rows (h, i) of one request:
+//   1. the request's budget plan (capped prefix / linear middle / floored suffix, tpd_budget.h) is solved
+//      by a 64-way parallel search: each lane evaluates one breakpoint predicate, a ballot picks the
+//      sub-interval, about log_64(n) rounds;
+//   2. per row, k_i comes from the closed form of the rounded prefix sums;
+//   3. the row's scores (j <= i, lane l holds j = l + 64 s) become order-preserving uint32 keys and the
+//      k-th largest key is found bit by bit (MSB first) with ballot + popcount counts;
+//   4. keys above the threshold are selected, then equal keys in increasing j until k are taken (ties go
+//      to the lower block index); each ballot is directly two 32-bit words of the packed mask row.
+// Bound: reading the causal half of the score rows (HBM) plus ~32 ballot rounds per row (ALU).
+#include "stem_internal.h"
+
+namespace stem {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 8;
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 is folded onto +0.
+__device__ __forceinline__ uint32_t ord_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of leading indices in [0, n) where pred holds (pred true on a prefix), via 64-ary search.
+// Indices are 32-bit (see the note on 64-bit compares in tpd_budget.h).
+template <typename Pred>
+__device__ __forceinline__ int32_t wave_prefix_count(int32_t n, int lane, Pred pred) {
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int32_t step = (hi - lo + 63) >> 6;
+    const int32_t x = lo + lane * step;
+    const bool t = (x < hi) && pred(x);
+    const int c = __popcll(__ballot(t));
+    if (c == 0) {
+      hi = lo;
+    } else {
+      lo = lo + (c - 1) * step + 1;
+      hi = min(hi, lo - 1 + step);
+    }
+  }
+  return lo;
+}
+
+__device__ TpdPlan wave_plan(int32_t n, const TopkArgs& a, int lane) {
+  TpdPlan s = tpd_plan_init(n, a.rho_num, a.rho_den, a.mu_num, a.mu_den);
+  const int32_t p = wave_prefix_count(n, lane, [&](int32_t i) { return tpd_capped(s, i); });
+  const int32_t q = wave_prefix_count(n, lane, [&](int32_t m) { return !tpd_floored(s, m); });
+  tpd_plan_finish(s, p, q);
+  return s;
+}
+
+template <int NS>
+__global__ __launch_bounds__(kWaves * 64) void topk_kernel(TopkArgs a) {
+  const int r = blockIdx.z;
+  const int h = blockIdx.y;
+  const int64_t cb = a.rt.cu_blocks[r];
+  const int n = a.rt.cu_blocks[r + 1] - (int)cb;
+  const int wave = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int i_begin = (blockIdx.x * kWaves + wave) * kRowsPerWave;
+  if (i_begin >= n) return;
+  const TpdPlan plan = wave_plan(n, a, lane);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int i_end = min(i_begin + kRowsPerWave, n);
+
+  for (int i = i_begin; i < i_end; ++i) {
+    const int64_t row = (int64_t)h * a.NB + cb + i;
+    const int k = (int)tpd_row_budget(plan, i);
+    const float* srow = a.scores + row * a.stride;
+    const int nslot = i / 64 + 1;
+    uint32_t key[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = lane + 64 * s;
+      key[s] = (s < nslot && j <= i) ? ord_key(srow[j]) : 0u;
+    }
+    // k-th largest key: the largest tau with #{key >= tau} >= k (valid keys are >= 0x007FFFFF > 0)
+    uint32_t tau = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tau | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        if (s < nslot) cnt += __popcll(__ballot(key[s] >= cand));
+      if (cnt >= k) tau = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (s < nslot) gt += __popcll(__ballot(key[s] > tau));
+    const int need = k - gt;
+    int taken = 0;
+    uint32_t* mrow = a.mask + row * a.mask_words;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s < nslot) {
+        const uint64_t eq = __ballot(key[s] == tau);
+        const int rank = taken + __popcll(eq & below);
+        const bool sel = key[s] > tau || (key[s] == tau && rank < need);
+        const uint64_t selm = __ballot(sel);
+        taken += __popcll(eq);
+        if (lane < 2 && 2 * s + lane < a.mask_words)
+          mrow[2 * s + lane] = lane == 0 ? (uint32_t)selm : (uint32_t)(selm >> 32);
+      }
+    }
+    for (int w = 2 * nslot + lane; w < a.mask_words; w += 64) mrow[w] = 0u;
+    if (lane == 0) a.counts[row] = k;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, int max_n, int num_reqs, hipStream_t s) {
+  const int rows_per_wg = kWaves * kRowsPerWave;
+  dim3 grid((unsigned)((max_n + rows_per_wg - 1) / rows_per_wg), (unsigned)a.hq, (unsigned)num_reqs);
+  dim3 block(kWaves * 64);
+  if (max_n <= 64) hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, a);
+  else if (max_n <= 128) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, a);
+  else if (max_n <= 256) hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, a);
+  else if (max_n <= 512) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, a);
+  else if (max_n <= 1024) hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, a);
+  else if (max_n <= 2048) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(topk_kernel<64>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace stem

@@ -1,0 +1,200 @@
+"""Host-side tests of the C-ABI library (no GPU): loading, exported symbols, the budget arithmetic shared
+with the selection kernel, workspace sizing, and every argument-validation error path.
+
+Calls here either touch no device memory (host helpers) or are built to fail validation, which happens on
+the host before any HIP call; fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import random
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_oam_amd as stem
+from block_sparse_attention_oam_amd import _abi
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stem.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_compiles_as_c99():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(stem.EXPORTS)
+    L = stem.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", stem.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(declared) <= exported
+
+
+def test_status_strings():
+    L = stem.lib()
+    for s, name in [(0, "STEM_OK"), (-1, "STEM_E_INVALID_ARG"), (-2, "STEM_E_UNSUPPORTED"),
+                    (-3, "STEM_E_WORKSPACE"), (-4, "STEM_E_HIP")]:
+        assert L.stem_status_string(s).decode() == name
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 16, 32, 64, 100, 256, 511, 1024])
+@pytest.mark.parametrize("rho", [(0, 1), (1, 100), (10, 100), (25, 100), (50, 100), (1, 1), (2, 7)])
+@pytest.mark.parametrize("mu", [(7, 10), (1, 1), (1, 2), (1, 100), (699, 1000)])
+def test_budget_arithmetic_matches_oracle(n, rho, mu):
+    got = stem.stem_tpd_budgets_host(n, *rho, *mu)
+    ref = oracle.tpd_budgets(n, *rho, *mu)
+    assert np.array_equal(got, ref)
+
+
+def test_budget_arithmetic_random_sweep():
+    rnd = random.Random(7)
+    for _ in range(150):
+        n = rnd.randint(1, 900)
+        rho = (rnd.randint(0, 100), 100)
+        mu = (rnd.randint(1, 20), 20)
+        assert np.array_equal(stem.stem_tpd_budgets_host(n, *rho, *mu), oracle.tpd_budgets(n, *rho, *mu))
+
+
+def test_budget_argument_errors():
+    for args in [(0, 1, 4, 7, 10), (8, -1, 4, 7, 10), (8, 5, 4, 7, 10), (8, 1, 0, 7, 10), (8, 1, 4, 0, 10),
+                 (8, 1, 4, 11, 10), (8, 1, 4, 7, 0), (40000, 1, 4, 7, 10 ** 6)]:
+        with pytest.raises(stem.StemError) as e:
+            stem.stem_tpd_budgets_host(*args)
+        assert e.value.status in (_abi.STEM_E_INVALID_ARG, _abi.STEM_E_UNSUPPORTED)
+
+
+# ------------------------------------------------------------------------------------------------ problems
+def _prob(**kw):
+    base = dict(cu_seqlens=[0, 1000, 3000], hq=8, hkv=2, head_dim=128, block=128, dtype="bf16")
+    base.update(kw)
+    return stem.make_problem(**base)
+
+
+def test_block_counts_and_workspace_layout():
+    p = _prob()
+    nb, mx = stem.block_counts(p)
+    assert (nb, mx) == (8 + 16, 16)
+    oq, ok, om = stem.workspace_layout(p)
+    qb = 8 * nb * 128 * 4
+    kb = 2 * nb * 128 * 4
+    mb = 2 * nb * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert (oq, ok, om) == (0, al(qb), al(qb) + al(kb))
+    assert stem.workspace_bytes(p) == al(qb) + al(kb) + al(mb)
+    p64 = _prob(cu_seqlens=[0, 65], block=64, head_dim=64, dtype="f32", hq=2, hkv=2)
+    assert stem.block_counts(p64) == (2, 2)
+
+
+class _FakeTensor:
+    """Stands in for a device tensor in calls that must fail validation: address and shape only."""
+
+    def __init__(self, addr=0x10000, shape=(1,), elem=4):
+        self._a, self.shape, self._e = addr, shape, elem
+
+    def data_ptr(self):
+        return self._a
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def element_size(self):
+        return self._e
+
+
+BAD_PROBLEMS = [
+    (dict(cu_seqlens=[0]), "num_reqs"),
+    (dict(cu_seqlens=[1, 10]), "cu_seqlens[0]"),
+    (dict(cu_seqlens=[0, 10, 5]), "decreases"),
+    (dict(cu_seqlens=[0, 0]), "empty"),
+    (dict(hq=6, hkv=4), "hq % hkv"),
+    (dict(hq=0), "hq"),
+    (dict(head_dim=96), "head_dim"),
+    (dict(block=32), "block"),
+    (dict(dtype=7), "dtype"),
+    (dict(dtype="fp8"), "scale"),
+    (dict(cu_seqlens=list(range(0, 258))), "num_reqs"),
+]
+
+
+@pytest.mark.parametrize("kw,msg", BAD_PROBLEMS)
+def test_invalid_problem_is_rejected_by_every_entry_point(kw, msg):
+    p = _prob(**kw)
+    T = _FakeTensor
+    calls = [
+        lambda: stem.block_counts(p),
+        lambda: stem.workspace_layout(p),
+        lambda: stem.stem_score(p, T(), T(), T(), 0.2, T(shape=(1, 1, 64)), T(shape=(1 << 30,), elem=1), stream=0),
+        lambda: stem.stem_tpd_topk(p, T(shape=(1, 1, 64)), (1, 4), (7, 10), T(shape=(1, 1, 2)), T(), stream=0),
+        lambda: stem.bsa_prefill(p, T(), T(), T(), None, T(), stream=0),
+    ]
+    for c in calls:
+        with pytest.raises(stem.StemError) as e:
+            c()
+        assert e.value.status in (_abi.STEM_E_INVALID_ARG, _abi.STEM_E_UNSUPPORTED)
+        assert msg in str(e.value)
+    assert stem.lib().stem_workspace_bytes(p.ref) == 0
+
+
+def test_paged_descriptor_errors():
+    pt = _FakeTensor(shape=(2, 16))
+    for kw, msg in [(dict(page_size=0), "page_size"), (dict(page_size=24), "page_size"),
+                    (dict(page_size=64, num_pages=0), "num_pages"),
+                    (dict(page_size=64, num_pages=10, page_table=_FakeTensor(shape=(2, 4))), "page_table_stride")]:
+        args = dict(page_table=pt, num_pages=10)
+        args.update(kw)
+        p = _prob(**args)
+        with pytest.raises(stem.StemError) as e:
+            stem.block_counts(p)
+        assert msg in str(e.value)
+
+
+def test_call_argument_errors():
+    p = _prob()  # NB = 24, max_n = 16
+    T = _FakeTensor
+    ws_need = stem.workspace_bytes(p)
+    cases = [
+        (lambda: stem.stem_score(p, T(), T(), T(), 0.2, T(shape=(8, 24, 15)), T(shape=(ws_need,), elem=1), stream=0),
+         "score_row_stride"),
+        (lambda: stem.stem_score(p, T(), T(), T(), 0.2, T(shape=(8, 24, 16)), T(shape=(ws_need - 1,), elem=1),
+                                 stream=0), "workspace"),
+        (lambda: stem.stem_score(p, T(addr=0x10008), T(), T(), 0.2, T(shape=(8, 24, 16)),
+                                 T(shape=(ws_need,), elem=1), stream=0), "aligned"),
+        (lambda: stem.stem_score(p, T(), T(), T(), float("nan"), T(shape=(8, 24, 16)), T(shape=(ws_need,), elem=1),
+                                 stream=0), "beta"),
+        (lambda: stem.stem_tpd_topk(p, T(shape=(8, 24, 16)), (1, 4), (7, 10), T(shape=(8, 24, 0)), T(), stream=0),
+         "mask_row_words"),
+        (lambda: stem.stem_tpd_topk(p, T(shape=(8, 24, 16)), (5, 4), (7, 10), T(shape=(8, 24, 1)), T(), stream=0),
+         "rho"),
+        (lambda: stem.stem_tpd_topk(p, T(shape=(8, 24, 16)), (1, 4), (0, 10), T(shape=(8, 24, 1)), T(), stream=0),
+         "mu"),
+        (lambda: stem.bsa_prefill(p, T(), T(), T(), T(shape=(8, 24, 0)), T(), stream=0), "mask_row_words"),
+        (lambda: stem.bsa_prefill(p, T(), T(), T(), None, T(), softmax_scale=float("inf"), stream=0),
+         "softmax_scale"),
+        (lambda: stem.bsa_prefill(p, T(), T(), T(), None, None, stream=0), "non-NULL"),
+    ]
+    for c, msg in cases:
+        with pytest.raises(stem.StemError) as e:
+            c()
+        assert msg in str(e.value), str(e.value)
+
+
+def test_last_error_is_cleared_by_a_successful_call():
+    with pytest.raises(stem.StemError):
+        stem.block_counts(_prob(hq=3, hkv=2))
+    assert stem.lib().stem_last_error().decode() != ""
+    stem.block_counts(_prob())
+    assert stem.lib().stem_last_error().decode() == ""

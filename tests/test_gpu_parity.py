@@ -1,0 +1,264 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Small cases (several tiles, ragged tails, GQA 1/4/8, paged with 16/32/64-token pages, fp32/bf16/fp8,
+external masks with empty rows) are checked on every output; the full-size workloads are checked on all
+budgets and selections and on sampled attention rows.  Selections must be bit-exact except in near-tie rows
+(k-th and (k+1)-th oracle scores within 1e-5 relative); attention given the oracle's mask must meet the
+max/mean abs tolerances of its dtype.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+import oracle
+from tests import stem_cases as sc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_oam_amd as stem  # noqa: F401  (fails loudly if libstem.so is missing)
+
+    stem.lib()
+    return torch.device("cuda:0")
+
+
+def _run(p, x, dev, masks_for_bsa=None, dense=False):
+    """Run the three stages on the GPU.  masks_for_bsa: per-request bool masks to feed bsa_prefill
+    (the oracle's); None uses the GPU's own selection.  Returns a dict of host arrays."""
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    kw = {}
+    if p.dtype == "fp8":
+        kw = dict(q_scale=upload(x["q_scale"]), k_scale=upload(x["k_scale"]), v_scale=upload(x["v_scale"]))
+    if p.paged:
+        pt = upload(x["page_table"])
+        prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype, page_table=pt,
+                                 page_size=p.page_size, num_pages=x["k_pages"].shape[0], **kw)
+        k, v = upload(x["k_pages"]), upload(x["v_pages"])
+    else:
+        prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype, **kw)
+        k, v = upload(x["k"]), upload(x["v"])
+    q = upload(x["q"])
+    L = StemPrefill(prob, dev)
+    L.score(q, k, v, p.beta)
+    L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
+    res = {}
+    qb, kb, M = L.pooled()
+    torch.cuda.synchronize()
+    res["qbar"], res["kbar"], res["M"] = qb.cpu().numpy(), kb.cpu().numpy(), M.cpu().numpy()
+    res["scores"] = L.scores.cpu().numpy()
+    res["words"] = L.mask.cpu().numpy().view(np.uint32)
+    res["counts"] = L.counts.cpu().numpy()
+    if masks_for_bsa is not None:
+        full = np.zeros((p.hq, L.NB, L.words), dtype=np.int32)
+        cb = p.cu_blocks
+        for r, m in enumerate(masks_for_bsa):
+            full[:, cb[r]:cb[r + 1]] = sc.pack_mask(m, L.words)
+        ext = upload(full)
+        L.attend(q, k, v, mask=ext)
+    else:
+        L.attend(q, k, v, mask=None if dense else "selected")
+    torch.cuda.synchronize()
+    res["out"] = L.out.float().cpu().numpy().astype(np.float64)
+    res["lse"] = L.lse.cpu().numpy().astype(np.float64)
+    res["NB"] = L.NB
+    return res
+
+
+def _check_stage1(p, g, ref):
+    cb = p.cu_blocks
+    worst_s = 0.0
+    for r, (qbar, kbar, M, S) in enumerate(ref):
+        sl = slice(cb[r], cb[r + 1])
+        assert np.max(np.abs(g["qbar"][:, sl] - qbar)) < 1e-5
+        assert np.max(np.abs(g["kbar"][:, sl] - kbar)) < 1e-5
+        assert np.max(np.abs(g["M"][:, sl] - M)) < 1e-5
+        n = S.shape[1]
+        tri = np.tril(np.ones((n, n), dtype=bool))
+        gs = g["scores"][:, sl, :n]
+        err = np.abs(gs - S)[:, tri] / np.maximum(1.0, np.abs(S[:, tri]))
+        worst_s = max(worst_s, float(err.max()))
+    assert worst_s < 2e-6, worst_s  # well inside the 1e-5 selection tie window
+    return worst_s
+
+
+SMALL = [
+    ("tiny_f32", {}),
+    ("tiny_f32", dict(lens=(1000,), hq=4, hkv=1)),
+    ("llama_32k_bf16", dict(lens=(1000,), hq=8, hkv=2)),
+    ("llama_32k_bf16", dict(lens=(300, 1, 129, 700), hq=4, hkv=4)),
+    ("llama_32k_bf16", dict(lens=(777,), hq=8, hkv=1, d=64)),
+    ("llama_32k_bf16", dict(lens=(640,), hq=4, hkv=2, block=64)),
+    ("llama_32k_bf16", dict(lens=(1500,), hq=4, hkv=1, rho_num=50, mu_num=1, mu_den=1)),
+    ("w8a8_128k_fp8", dict(lens=(1000,), hq=8, hkv=2)),
+    ("w8a8_128k_fp8", dict(lens=(200, 513), hq=4, hkv=1, d=64)),
+    ("paged_ragged_bf16", dict(lens=(300, 64, 700), hq=4, hkv=2)),
+    ("paged_ragged_bf16", dict(lens=(257, 1000), hq=4, hkv=1, page_size=16)),
+    ("paged_ragged_bf16", dict(lens=(129, 500), hq=2, hkv=2, page_size=32, dtype="fp8")),
+]
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_small_case_all_outputs(dev, name, over):
+    p = synth.make_problem(name, **over)
+    _log(f"[case] {name} {over}")
+    x = synth.make_inputs(p, seed=0)
+    ref1 = sc.oracle_stage1(p, x)
+    budgets = sc.oracle_budgets(p)
+    masks = sc.oracle_masks([s for *_, s in ref1], budgets)
+    g = _run(p, x, dev, masks_for_bsa=masks)
+    worst = _check_stage1(p, g, ref1)
+    ties = sc.check_selection(p, [s for *_, s in ref1], budgets, g["words"], g["counts"])
+    ora = sc.oracle_attention(p, x, masks)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
+    tmax, tmean = sc.TOL[p.dtype]
+    _log(f"  score rel err {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
+    assert mx <= tmax and mean <= tmean
+    assert lerr <= 10 * tmax
+
+
+@pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[7], SMALL[9]],
+                         ids=["f32", "bf16", "fp8", "paged"])
+def test_dense_mode_matches_textbook_attention(dev, name, over):
+    """mask = NULL runs dense causal attention: the 100%-budget special case of the oracle."""
+    p = synth.make_problem(name, **over)
+    x = synth.make_inputs(p, seed=1)
+    g = _run(p, x, dev, dense=True)
+    ora = sc.oracle_attention(p, x, None)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
+    _log(f"[dense] {name}: out max {mx:.2e} mean {mean:.2e} lse {lerr:.2e}")
+    tmax, tmean = sc.TOL[p.dtype]
+    assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+
+
+def test_end_to_end_gpu_selection_feeds_attention(dev):
+    p = synth.make_problem("llama_32k_bf16", lens=(1200, 333), hq=8, hkv=2)
+    x = synth.make_inputs(p, seed=2)
+    g = _run(p, x, dev)
+    cb = p.cu_blocks
+    gmasks = [sc.unpack_mask(g["words"][:, cb[r]:cb[r + 1]], p.nblocks(r)) for r in range(len(p.lens))]
+    for m in gmasks:
+        m &= np.tril(np.ones(m.shape[1:], dtype=bool))[None]
+    ora = sc.oracle_attention(p, x, gmasks)
+    mx, mean, _ = sc.compare_attention(p, ora, g["out"], g["lse"])
+    assert mx <= 2e-2 and mean <= 2e-3
+
+
+def test_external_mask_with_empty_rows_and_skipped_diagonal(dev):
+    p = synth.make_problem("llama_32k_bf16", lens=(900, 260), hq=4, hkv=2)
+    x = synth.make_inputs(p, seed=3)
+    rng = np.random.default_rng(4)
+    masks = []
+    for r in range(len(p.lens)):
+        n = p.nblocks(r)
+        m = rng.random((p.hq, n, n)) < 0.4
+        m[0, :, :] = False  # head 0: every row empty
+        m[1, np.arange(n), np.arange(n)] = False  # head 1: diagonal never selected
+        m[2, :, :] = True  # head 2: dense, plus bits past the diagonal that must be ignored
+        masks.append(m)
+    g = _run(p, x, dev, masks_for_bsa=masks)
+    tri = [m & np.tril(np.ones(m.shape[1:], dtype=bool))[None] for m in masks]
+    ora = sc.oracle_attention(p, x, tri)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
+    assert mx <= 2e-2 and mean <= 2e-3
+    a, b = sc.request_slices(p)[0]
+    assert np.all(g["out"][a:b, 0] == 0) and np.all(np.isneginf(g["lse"][0, a:b]))
+
+
+def test_repeated_runs_are_bitwise_identical(dev):
+    p = synth.make_problem("llama_32k_bf16", lens=(2000,), hq=8, hkv=2)
+    x = synth.make_inputs(p, seed=5)
+    g1 = _run(p, x, dev)
+    g2 = _run(p, x, dev)
+    for key in ("scores", "words", "counts", "out", "lse"):
+        a, b = g1[key], g2[key]
+        if key == "scores":
+            n = p.nblocks(0)
+            tri = np.tril(np.ones((n, n), dtype=bool))
+            a, b = a[:, :, :n][:, tri], b[:, :, :n][:, tri]
+        assert np.array_equal(a, b, equal_nan=True), key
+
+
+# ------------------------------------------------------------------------------------ full-size workloads
+FULL = ["tiny_f32", "llama_32k_bf16", "llama_128k_bf16", "w8a8_128k_fp8", "paged_ragged_bf16"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload(dev, name):
+    """All budgets and selections bit-exact (tie window aside); attention on sampled rows with the oracle's
+    mask; the dense mode on sampled rows."""
+    p = synth.make_problem(name)
+    _log(f"[full] {name}: generating inputs")
+    x = synth.make_inputs(p, seed=0)
+    _log(f"[full] {name}: oracle scores and selection")
+    ref1 = sc.oracle_stage1(p, x)
+    S_list = [s for *_, s in ref1]
+    budgets = sc.oracle_budgets(p)
+    masks = sc.oracle_masks(S_list, budgets)
+    _log(f"[full] {name}: GPU run")
+    g = _run(p, x, dev, masks_for_bsa=masks)
+    worst = _check_stage1(p, g, ref1)
+    ties = sc.check_selection(p, S_list, budgets, g["words"], g["counts"])
+    rows = [sc.sample_rows(p, r, 12) if p.lens[r] > 4096 else None for r in range(len(p.lens))]
+    _log(f"[full] {name}: oracle attention on sampled rows")
+    ora = sc.oracle_attention(p, x, masks, rows)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
+    _log(f"[full] {name}: score rel {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, "
+         f"lse {lerr:.2e}")
+    tmax, tmean = sc.TOL[p.dtype]
+    assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+
+
+# ------------------------------------------------------------------------------------ budgets on the device
+BUDGET_SWEEP = [(n, rho, mu) for n in (1, 2, 3, 5, 12, 31, 32, 33, 64, 65, 100, 255, 256, 1000, 1024, 2048, 4096)
+                for rho in ((25, 100), (10, 100), (50, 100), (100, 100), (1, 100), (1, 3))
+                for mu in ((7, 10), (1, 1), (1, 2), (1, 100))]
+
+
+def test_device_budgets_and_exact_ties_match_oracle(dev):
+    """stem_tpd_topk on all-equal scores: counts are the TPD budgets (exact integers) and every row selects
+    its k lowest block indices (ties go to the lower index).  Ragged batches exercise per-request plans."""
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import upload
+
+    groups = {}
+    for n, rho, mu in BUDGET_SWEEP:
+        groups.setdefault((rho, mu), []).append(n)
+    for (rho, mu), ns in groups.items():
+        for batch in (ns[:9], ns[9:]):
+            lens = [64 * n for n in batch]
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            prob = stem.make_problem(cu, 1, 1, 64, 64, "f32")
+            NB, mx = stem.block_counts(prob)
+            W = (mx + 31) // 32
+            scores = torch.zeros((1, NB, mx), dtype=torch.float32, device=dev)
+            mask = torch.full((1, NB, W), -1, dtype=torch.int32, device=dev)
+            counts = torch.zeros((1, NB), dtype=torch.int32, device=dev)
+            stem.stem_tpd_topk(prob, scores, rho, mu, mask, counts)
+            torch.cuda.synchronize()
+            c = counts.cpu().numpy()[0]
+            words = mask.cpu().numpy()[0].view(np.uint32)
+            off = 0
+            for n in batch:
+                ref = oracle.tpd_budgets(n, *rho, *mu)
+                assert np.array_equal(c[off:off + n], ref), (n, rho, mu)
+                bits = sc.unpack_mask(words[off:off + n], W * 32)
+                want = np.arange(W * 32)[None, :] < ref[:, None]
+                assert np.array_equal(bits, want), (n, rho, mu)
+                off += n

@@ -132,7 +132,7 @@ def _float_bisect_x(n, T, mu):
     def F(x):
         return np.minimum(np.maximum(x * w, 1.0), i1).sum()
 
-    lo, hi = 0.0, float(n) / max(mu, 1e-9) + n + 1.0
+    lo, hi = 0.0, float(n) / mu + n + 1.0
     for _ in range(200):
         mid = 0.5 * (lo + hi)
         if F(mid) < T:
@@ -156,7 +156,7 @@ def test_tpd_total_closed_forms():
 
 @pytest.mark.parametrize("n,rho", [(2, (1, 2)), (7, (1, 4)), (32, (25, 100)), (64, (10, 100)),
                                    (100, (37, 100)), (256, (25, 100)), (33, (90, 100)), (513, (1, 100))])
-@pytest.mark.parametrize("mu", [(7, 10), (1, 1), (1, 2), (0, 1), (1, 3)])
+@pytest.mark.parametrize("mu", [(7, 10), (1, 1), (1, 2), (1, 100), (1, 3)])
 def test_tpd_budget_invariants(n, rho, mu):
     T = oracle.tpd_total(n, *rho)
     x, rs = oracle.tpd_solve(n, T, Fraction(*mu))
@@ -183,6 +183,11 @@ def test_tpd_full_budget_is_dense_and_min_budget_is_one_per_row():
     for n in (1, 2, 5, 40):
         assert np.array_equal(oracle.tpd_budgets(n, 1, 1, 7, 10), np.arange(1, n + 1))
         assert np.array_equal(oracle.tpd_budgets(n, 0, 1, 7, 10), np.ones(n, dtype=np.int64))
+
+
+def test_tpd_rejects_mu_zero():
+    with pytest.raises(ValueError):
+        oracle.tpd_budgets(8, 1, 2, 0, 1)
 
 
 def test_tpd_uniform_when_mu_is_one():
