@@ -194,6 +194,8 @@ def tpd_solve(n: int, T: int, mu: Fraction):
     at most the i+1 causal blocks; x = k_start is chosen so the rows add up to T.  F(x) = sum_i r_i(x) is
     continuous, piecewise linear and nondecreasing, so x* is found between two adjacent breakpoints.
     """
+    if not (0 < mu <= 1):
+        raise ValueError("mu must lie in (0, 1]: with mu = 0 the last row could never reach its share")
     if n == 1:
         return Fraction(1), [Fraction(1)]
     w = [1 - (1 - mu) * Fraction(i, n - 1) for i in range(n)]
@@ -206,9 +208,8 @@ def tpd_solve(n: int, T: int, mu: Fraction):
 
     bps = set()
     for i in range(n):
-        if w[i] > 0:
-            bps.add(1 / w[i])
-            bps.add((i + 1) / w[i])
+        bps.add(1 / w[i])
+        bps.add((i + 1) / w[i])
     bps = sorted(bps)
     # F(0) = n (every row floored at 1); F is flat on [0, bps[0]].
     lo, hi = 0, len(bps) - 1
