@@ -1,0 +1,354 @@
+// Block-sparse causal flash attention, bf16 inputs, head_dim 128, block 128 (the main production shape).
+//
+// Source: "从Stem稀疏注意力看大模型推理的架构取舍", section "HPC-BSA：跳块零开销的秘密" (per query block: keep the
+// mask row on chip, build the list of KV blocks, iterate only over the list with the dense inner loop;
+// skipped blocks act as -inf scores; K/V may sit in pages behind a page table) and section "答案不在算法里"
+// (the fixed block size is what lets the decision leave the inner loop).
+//
+// Same mathematics and work decomposition as the generic kernel (bsa_fwd.hip); this version is shaped for
+// gfx950's issue limits, because the generic one spends ~24 VALU instructions per MFMA:
+//  * K and V sub-tiles (64 keys x 128 dims, 16 KB each) go from global memory straight into LDS with
+//    global_load_lds_dwordx4 (lane l of an instruction fills the l-th 16-byte slot of a 1 KB LDS chunk):
+//    no staging registers, no LDS store or repacking instructions.  The loads of sub-tile u+1 are issued
+//    after the barrier of sub-tile u and overlap its compute (double buffer, one barrier per sub-tile).
+//  * tiles are row-major without padding; 16-byte slots are XOR-swizzled by row (K: slot ^ (row & 7),
+//    V: slot ^ 2*(row & 3)), which the loading lanes apply by choosing their source chunk, so the MFMA
+//    operand reads below are free of LDS bank conflicts.
+//  * S^T = K Q^T (v_mfma_f32_32x32x16_bf16): K operand = one ds_read_b128 per MFMA.  O^T = V^T P^T: the V^T
+//    operand is gathered from the row-major V tile by two ds_read_b64_tr_b16 (transposing 16-bit reads),
+//    in the key order that the S^T accumulator layout gives P^T, so P never moves between lanes.
+//  * softmax: raw v_exp_f32 (no denormal fix-up), one FMA folds the scale and the running max, the row
+//    max is one v_permlane32_swap away, and the O^T rescale is lazy: the reference max is only raised
+//    when a tile's max exceeds it by more than 2^8 (exact arithmetic with a different reference point;
+//    p <= 256 fits bf16), so after the first blocks the rescale is skipped.
+//  * per-thread global offsets are computed once; each sub-tile only changes a uniform base address
+//    (contiguous K/V, or pages of >= 64 tokens); small pages look up one page per row.  The diagonal block
+//    takes a separate path with the causal mask; other blocks have no per-element compares.
+#include "stem_internal.h"
+
+namespace stem {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int B = 128;
+constexpr int KT = 64;
+constexpr int NT = 256;
+constexpr int TILE = KT * D * 2;  // bytes per K or V sub-tile
+constexpr int kMaxList = 2048;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+
+// Two floats -> packed bf16 pair (round to nearest even) with one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// PAGE: 0 contiguous K/V, 1 pages of a multiple of 64 tokens (one page per sub-tile), 2 smaller pages.
+template <int PAGE, bool MASKED>
+__global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
+  // Two buffers, each its own LDS object, so the loads into one are known not to alias reads of the other.
+  __shared__ __align__(1024) uint8_t kbuf0[TILE], vbuf0[TILE], kbuf1[TILE], vbuf1[TILE];
+  __shared__ uint16_t list[MASKED ? kMaxList : 1];
+  __shared__ int list_len;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- work item (same order as the generic kernel: XCD-aware, KV-head-major, longest rows first)
+  const int grp = a.hq / a.hkv;
+  int64_t logical = blockIdx.x;
+  if (a.xcd_remap) {
+    const int64_t per = (int64_t)gridDim.x / 8;
+    logical = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  }
+  const int64_t per_g = a.NB * grp;
+  const int g = (int)(logical / per_g);
+  const int64_t rem = logical % per_g;
+  const int64_t ib = a.NB - 1 - rem / grp;
+  const int h = g * grp + (int)(rem % grp);
+  const int r = find_request(a.rt, (int)ib);
+  const int i = (int)ib - a.rt.cu_blocks[r];
+  const int tb = a.rt.cu_seqlens[r];
+  const int L = a.rt.cu_seqlens[r + 1] - tb;
+
+  // ---- list of selected blocks
+  int nsel;
+  if constexpr (MASKED) {
+    if (wave == 0) {
+      const uint32_t* mrow = a.mask + ((int64_t)h * a.NB + ib) * a.mask_words;
+      const int nwords = (i >> 5) + 1;
+      int base = 0;
+      for (int w0 = 0; w0 < nwords; w0 += 64) {
+        const int w = w0 + lane;
+        uint32_t word = 0;
+        if (w < nwords) {
+          word = mrow[w];
+          if (w == nwords - 1) {
+            const int nb = (i & 31) + 1;
+            word &= (nb == 32) ? 0xFFFFFFFFu : ((1u << nb) - 1u);
+          }
+        }
+        const int c = __popc(word);
+        int incl = c;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        int pos = base + incl - c;
+        while (word) {
+          const int bit = __ffs(word) - 1;
+          list[pos++] = (uint16_t)(w * 32 + bit);
+          word &= word - 1;
+        }
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) list_len = base;
+    }
+    __syncthreads();
+    nsel = list_len;
+  } else {
+    nsel = i + 1;
+  }
+  const int nsub = nsel * 2;
+
+  // ---- Q fragments (B operand of S^T = K Q^T)
+  const int qr = wave * 32 + l32;
+  const int qpos = i * B + qr;
+  const bool qvalid = qpos < L;
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)(tb + qpos) * a.hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 w = qvalid ? *(const uint4*)(qp + 16 * kk + 8 * half) : make_uint4(0u, 0u, 0u, 0u);
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  // ---- loader geometry: instruction m of this wave fills LDS chunk (4*wave + m) = tile rows
+  //      16*wave + 4*m + lane/16, slot lane & 15 (16 bytes); the lane fetches the swizzled source chunk.
+  const int64_t row_stride = (int64_t)a.hkv * D * 2;
+  int ldrow[4], kchunk[4], vchunk[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = 16 * wave + 4 * m + (lane >> 4);
+    const int slot = lane & 15;
+    ldrow[m] = row;
+    kchunk[m] = slot ^ (row & 7);
+    vchunk[m] = slot ^ (2 * (row & 3));
+  }
+  const uint8_t* kbase_all = (const uint8_t*)a.k;
+  const uint8_t* vbase_all = (const uint8_t*)a.v;
+  const int64_t head_off = (int64_t)g * D * 2;
+
+  auto sub_key0 = [&](int u) -> int {
+    const int j = MASKED ? (int)list[u >> 1] : (u >> 1);
+    return j * B + (u & 1) * KT;
+  };
+
+  auto issue_loads = [&](int u, uint8_t* kdst, uint8_t* vdst) {
+    const int kp0 = sub_key0(u);
+    if (kp0 >= L) return;  // a second half-block past the end of the request: nothing to load
+    lds_u8* kl = (lds_u8*)kdst + wave * 4096;
+    lds_u8* vl = (lds_u8*)vdst + wave * 4096;
+    const bool full = kp0 + KT <= L;
+    if (PAGE == 0 || PAGE == 1) {
+      int64_t tok0;  // token index (pool row) of the sub-tile's first key
+      if (PAGE == 0) {
+        tok0 = (int64_t)tb + kp0;
+      } else {
+        const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp0 / a.kv.page_size];
+        tok0 = (int64_t)page * a.kv.page_size + (kp0 % a.kv.page_size);
+      }
+      const int64_t base = tok0 * row_stride + head_off;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        int row = ldrow[m];
+        if (!full) row = min(row, L - 1 - kp0);  // keys past the end repeat the last key (masked anyway)
+        const int64_t off = base + (int64_t)row * row_stride;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase_all + off + kchunk[m] * 16), kl + m * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase_all + off + vchunk[m] * 16), vl + m * 1024, 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int kp = min(kp0 + ldrow[m], L - 1);
+        const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp / a.kv.page_size];
+        const int64_t off =
+            ((int64_t)page * a.kv.page_size + (kp % a.kv.page_size)) * row_stride + head_off;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase_all + off + kchunk[m] * 16), kl + m * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase_all + off + vchunk[m] * 16), vl + m * 1024, 16, 0, 0);
+      }
+    }
+  };
+
+  // ---- operand read offsets (bytes inside a tile)
+  // K (A operand of S^T): row 32t + l32, chunk c = 2kk + half at slot c ^ (row & 7); row & 7 = l32 & 7.
+  uint32_t koffs[4];
+#pragma unroll
+  for (int k4 = 0; k4 < 4; ++k4) koffs[k4] = l32 * 256 + 16 * ((2 * k4 + half) ^ (l32 & 7));
+  // V^T (A operand of O^T) via transposing reads: source lane (G = lane/16, s = lane%16, rr = s/4, c = s%4)
+  // addresses row 16mm + 4*(G/2) + rr (+8 for the second read), dims 32dt + 16*(G&1) + 4c.
+  uint32_t voffs[4];
+  {
+    const int G = lane >> 4, s = lane & 15, rr = s >> 2, c = s & 3;
+    const int row0 = 4 * (G >> 1) + rr;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
+      voffs[dt] = row0 * 256 + 16 * (chunk ^ (2 * rr)) + 8 * (c & 1);
+    }
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) o[dt][x] = 0.f;
+  float m_run = -1e30f;  // reference max (log2 units); finite so masked rows never form inf - inf
+  float l_part = 0.f;
+  const float c2 = a.scale_log2;
+
+  // One sub-tile: wait for its loads, start the next sub-tile's loads into the other buffer, compute.
+  auto step = [&](int u, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (u + 1 < nsub) issue_loads(u + 1, knext, vnext);
+    const int kp0 = sub_key0(u);
+    if (kp0 >= L) return;
+    const bool diag = (kp0 / B) == i;
+    if (diag && kp0 > i * B + wave * 32 + 31) return;  // every key of this sub-tile is after the wave's rows
+    const lds_u8* Kt = (const lds_u8*)kcur;
+    const lds_u8* Vt = (const lds_u8*)vcur;
+    f32x16 s0, s1;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      s0[x] = 0.f;
+      s1[x] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint32_t off = koffs[kk & 3] + (kk >> 2) * 128;
+      const bf16x8 a0 = *(const __attribute__((address_space(3))) bf16x8*)(Kt + off);
+      const bf16x8 a1 = *(const __attribute__((address_space(3))) bf16x8*)(Kt + off + 32 * 256);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
+    }
+    if (diag) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int kl = 8 * (x >> 2) + 4 * half + (x & 3);
+        if (kp0 + kl > qpos) s0[x] = -INFINITY;
+        if (kp0 + 32 + kl > qpos) s1[x] = -INFINITY;
+      }
+    }
+    float mx = max3(s0[0], s0[1], s1[0]);
+    mx = max3(mx, s0[2], s1[1]);
+#pragma unroll
+    for (int x = 3; x < 16; ++x) mx = max3(mx, s0[x], s1[x - 1]);
+    mx = fmaxf(mx, s1[15]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mt = mx * c2;
+    if (__ballot(mt > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) o[dt][x] *= alpha;
+      m_run = m_new;
+    }
+    const float negm = -m_run;
+    float ps = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
+      s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
+      ps += s0[x] + s1[x];
+    }
+    l_part += ps;
+
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const f32x16& st = (mm < 2) ? s0 : s1;
+      const int x0 = 8 * (mm & 1);
+      const uint4 pw = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
+                                  cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const lds_u8* vp = Vt + voffs[dt] + mm * 4096;
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)vp);
+        const i16x4 v1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(vp + 2048));
+        const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+        const uint4 vw = make_uint4(w0.x, w0.y, w1.x, w1.y);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf, o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nsub > 0) issue_loads(0, kbuf0, vbuf0);
+  for (int u = 0; u < nsub; u += 2) {
+    step(u, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (u + 1 < nsub) step(u + 1, kbuf1, vbuf1, kbuf0, vbuf0);
+  }
+
+  // ---- epilogue
+  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+  if (!qvalid) return;
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  const int64_t ooff = ((int64_t)(tb + qpos) * a.hq + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * dt + 8 * rq + 4 * half;
+      *(uint2*)((uint16_t*)a.out + ooff + d0) =
+          make_uint2(cvt_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
+                     cvt_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv));
+    }
+  if (a.lse != nullptr && half == 0)
+    a.lse[(int64_t)h * a.tokens + tb + qpos] =
+        (l_tot > 0.f) ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+}
+
+}  // namespace
+
+bool bsa_bf16_supported(int dtype, int head_dim, int block) {
+  return dtype == STEM_BF16 && head_dim == D && block == B;
+}
+
+hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s) {
+  dim3 grid((unsigned)(a.hq * a.NB));
+  dim3 block(NT);
+  const int page_mode = !a.kv.paged ? 0 : (a.kv.page_size % KT == 0 ? 1 : 2);
+#define STEM_LAUNCH(PM)                                                                     \
+  do {                                                                                      \
+    if (masked) hipLaunchKernelGGL((bsa_bf16_kernel<PM, true>), grid, block, 0, s, a);      \
+    else hipLaunchKernelGGL((bsa_bf16_kernel<PM, false>), grid, block, 0, s, a);            \
+  } while (0)
+  if (page_mode == 0) STEM_LAUNCH(0);
+  else if (page_mode == 1) STEM_LAUNCH(1);
+  else STEM_LAUNCH(2);
+#undef STEM_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace stem
