@@ -11,14 +11,16 @@
 //    global_load_lds_dwordx4 (lane l of an instruction fills the l-th 16-byte slot of a 1 KB LDS chunk):
 //    no staging registers, no LDS store or repacking instructions.  The loads of sub-tile u+1 are issued
 //    after the barrier of sub-tile u and overlap its compute (double buffer, one barrier per sub-tile).
-//  * tiles are row-major without padding; 16-byte slots are XOR-swizzled by row (K: slot ^ (row & 7),
-//    V: slot ^ 2*(row & 3)), which the loading lanes apply by choosing their source chunk, so the MFMA
-//    operand reads below are free of LDS bank conflicts.
+//  * tiles are row-major without padding (a 256-byte row spans the 64 LDS banks once); 16-byte slots are
+//    XOR-swizzled by row (K: slot ^ (row & 15), V: slot ^ 4*(row & 3)), which the loading lanes apply by
+//    choosing their source chunk.  A ds_read_b128 pass (16 lanes, 16 consecutive K rows, one chunk) and a
+//    ds_read_b64_tr_b16 pass (32 lanes, 4 V rows x 4 chunks) then touch every bank once.
 //  * S^T = K Q^T (v_mfma_f32_32x32x16_bf16): K operand = one ds_read_b128 per MFMA.  O^T = V^T P^T: the V^T
 //    operand is gathered from the row-major V tile by two ds_read_b64_tr_b16 (transposing 16-bit reads),
 //    in the key order that the S^T accumulator layout gives P^T, so P never moves between lanes.
 //  * softmax: raw v_exp_f32 (no denormal fix-up), one FMA folds the scale and the running max, the row
-//    max is one v_permlane32_swap away, and the O^T rescale is lazy: the reference max is only raised
+//    max is one v_permlane32_swap away, the row sum is v_dot2_f32_bf16 over the rounded P pairs (the values
+//    that multiply V).  The O^T rescale is lazy: the reference max is only raised
 //    when a tile's max exceeds it by more than 2^8 (exact arithmetic with a different reference point;
 //    p <= 256 fits bf16), so after the first blocks the rescale is skipped.
 //  * per-thread global offsets are computed once; each sub-tile only changes a uniform base address
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     const int row = 16 * wave + 4 * m + (lane >> 4);
     const int slot = lane & 15;
     ldrow[m] = row;
-    kchunk[m] = slot ^ (row & 7);
-    vchunk[m] = slot ^ (2 * (row & 3));
+    kchunk[m] = slot ^ (row & 15);
+    vchunk[m] = slot ^ (4 * (row & 3));
   }
   const uint8_t* kbase_all = (const uint8_t*)a.k;
   const uint8_t* vbase_all = (const uint8_t*)a.v;
@@ -195,10 +197,10 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   };
 
   // ---- operand read offsets (bytes inside a tile)
-  // K (A operand of S^T): row 32t + l32, chunk c = 2kk + half at slot c ^ (row & 7); row & 7 = l32 & 7.
-  uint32_t koffs[4];
+  // K (A operand of S^T): row 32t + l32, chunk c = 2kk + half at slot c ^ (row & 15); row & 15 = l32 & 15.
+  uint32_t koffs[8];
 #pragma unroll
-  for (int k4 = 0; k4 < 4; ++k4) koffs[k4] = l32 * 256 + 16 * ((2 * k4 + half) ^ (l32 & 7));
+  for (int kk = 0; kk < 8; ++kk) koffs[kk] = l32 * 256 + 16 * ((2 * kk + half) ^ (l32 & 15));
   // V^T (A operand of O^T) via transposing reads: source lane (G = lane/16, s = lane%16, rr = s/4, c = s%4)
   // addresses row 16mm + 4*(G/2) + rr (+8 for the second read), dims 32dt + 16*(G&1) + 4c.
   uint32_t voffs[4];
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const int chunk = 4 * dt + 2 * (G & 1) + (c >> 1);
-      voffs[dt] = row0 * 256 + 16 * (chunk ^ (2 * rr)) + 8 * (c & 1);
+      voffs[dt] = row0 * 256 + 16 * (chunk ^ (4 * rr)) + 8 * (c & 1);
     }
   }
 
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t off = koffs[kk & 3] + (kk >> 2) * 128;
+      const uint32_t off = koffs[kk];
       const bf16x8 a0 = *(const __attribute__((address_space(3))) bf16x8*)(Kt + off);
       const bf16x8 a1 = *(const __attribute__((address_space(3))) bf16x8*)(Kt + off + 32 * 256);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
@@ -275,22 +277,35 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
       m_run = m_new;
     }
     const float negm = -m_run;
-    float ps = 0.f;
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
       s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
-      ps += s0[x] + s1[x];
     }
-    l_part += ps;
-
+    // P rounded to bf16 pairs; the row sum adds exactly these rounded values (v_dot2_f32_bf16 with (1, 1)).
+    uint4 pw[4];
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       const f32x16& st = (mm < 2) ? s0 : s1;
       const int x0 = 8 * (mm & 1);
-      const uint4 pw = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
-                                  cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      pw[mm] = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
+                          cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
+    }
+    {
+      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].x), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].y), ones, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].z), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].w), ones, ps1, false);
+      }
+      l_part += ps0 + ps1;
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[mm]);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const lds_u8* vp = Vt + voffs[dt] + mm * 4096;
