@@ -19,8 +19,7 @@
 //    operand is gathered from the row-major V tile by two ds_read_b64_tr_b16 (transposing 16-bit reads),
 //    in the key order that the S^T accumulator layout gives P^T, so P never moves between lanes.
 //  * softmax: raw v_exp_f32 (no denormal fix-up), one FMA folds the scale and the running max, the row
-//    max is one v_permlane32_swap away, the row sum is v_dot2_f32_bf16 over the rounded P pairs (the values
-//    that multiply V).  The O^T rescale is lazy: the reference max is only raised
+//    max is one v_permlane32_swap away, and the O^T rescale is lazy: the reference max is only raised
 //    when a tile's max exceeds it by more than 2^8 (exact arithmetic with a different reference point;
 //    p <= 256 fits bf16), so after the first blocks the rescale is skipped.
 //  * per-thread global offsets are computed once; each sub-tile only changes a uniform base address
@@ -277,13 +276,15 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
       m_run = m_new;
     }
     const float negm = -m_run;
+    float ps = 0.f;
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
       s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
+      ps += s0[x] + s1[x];
     }
-    // P rounded to bf16 pairs; the row sum adds exactly these rounded values (v_dot2_f32_bf16 with (1, 1)).
-    uint4 pw[4];
+    l_part += ps;
+    uint4 pw[4];  // P rounded to bf16 pairs, the B operand of each k-step
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       const f32x16& st = (mm < 2) ? s0 : s1;
@@ -291,18 +292,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
       pw[mm] = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
                           cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
     }
-    {
-      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
-      float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].x), ones, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].y), ones, ps1, false);
-        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].z), ones, ps0, false);
-        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].w), ones, ps1, false);
-      }
-      l_part += ps0 + ps1;
-    }
+
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[mm]);

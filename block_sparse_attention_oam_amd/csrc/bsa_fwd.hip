@@ -451,6 +451,7 @@ hipError_t launch2(const BsaArgs& a, int head_dim, bool masked, hipStream_t s) {
 
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int head_dim, bool /*paged*/, bool masked, hipStream_t s) {
   if (bsa_bf16_supported(dtype, head_dim, a.B)) return launch_bsa_bf16(a, masked, s);
+  if (bsa_fp8_supported(dtype, head_dim, a.B)) return launch_bsa_fp8(a, masked, s);
   if (dtype == STEM_F32) return launch2<4>(a, head_dim, masked, s);
   if (dtype == STEM_BF16) return launch2<2>(a, head_dim, masked, s);
   return launch2<1>(a, head_dim, masked, s);
