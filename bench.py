@@ -109,6 +109,23 @@ def time_bsa(L, q, k, v, mask, reps, torch):
     return a.elapsed_time(b) / reps
 
 
+def measure_other(name, steps, warmup, dev, torch):
+    """ms/layer and effective TFLOP/s of another workload (same step: score, select, attend)."""
+    import synth
+
+    p = synth.make_problem(name)
+    x = synth.make_inputs(p, seed=0)
+    L, q, k, v = setup(p, x, dev)
+    ms, stage, bsa_each = time_layer(L, q, k, v, p, steps, warmup, torch)
+    fl = 4 * p.d * visible_pairs(p, L.mask.cpu().numpy().view(np.uint32), L.NB)
+    bsa = float(np.mean(bsa_each))
+    peak = PEAK[p.dtype]
+    return {"workload": describe(p), "dtype": p.dtype, "ms_per_layer": round(ms, 4),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "pct_of_peak": round(100 * fl / (ms * 1e-3) / 1e12 / peak, 2),
+            "stages_ms": [round(float(t), 4) for t in stage], "bsa_tflops": round(fl / (bsa * 1e-3) / 1e12, 2),
+            "peak_tflops": peak}
+
+
 def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
     """The oracle, as it stands, on a bounded sample of rows of the same workload: for each sampled
     (query head, query block) row it pools, scores, takes the TPD budget, selects and attends.
@@ -179,7 +196,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_128k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the dense run, density sweep and 32K line")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense run, the density sweep and the other workloads")
+    ap.add_argument("--no-other-workloads", action="store_true", help="skip the 32K / fp8 / paged / fp32 lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -231,9 +250,10 @@ def main():
         "effective_flop_per_layer": flops,
     }
     # Roofline of the dominant kernel (block-sparse attention): effective flops / average launch time.
-    src = open(os.path.join(ROOT, "block_sparse_attention_oam_amd", "csrc", "bsa_fwd.hip"), "rb").read()
+    kernel_src = {"bf16": "bsa_bf16.hip", "fp8": "bsa_fp8.hip"}.get(p.dtype, "bsa_fwd.hip")
+    src = open(os.path.join(ROOT, "block_sparse_attention_oam_amd", "csrc", kernel_src), "rb").read()
     sha = hashlib.sha256(src).hexdigest()
-    out["roofline"] = {"kernel": "bsa_kernel", "bound": "mfma", "achieved": round(bsa_tflops, 2), "peak": peak,
+    out["roofline"] = {"kernel": kernel_src.replace(".hip", "_kernel"), "bound": "mfma", "achieved": round(bsa_tflops, 2), "peak": peak,
                        "unit": "TFLOP/s", "frac": round(bsa_tflops / peak, 4),
                        "traffic": traffic_from_profile(sha), "avg_launch_ms": round(bsa_ms, 4)}
     if not args.no_extras:
@@ -254,17 +274,13 @@ def main():
                                "density": round(f2 / (4 * p.d * dense_pairs(p)), 4)}
         out["density_sweep"] = sweep
         L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
-        if args.workload == "llama_128k_bf16":
-            log("[bench] 32K workload")
-            p32 = synth.make_problem("llama_32k_bf16")
-            x32 = synth.make_inputs(p32, seed=0)
-            L32, q32, k32, v32 = setup(p32, x32, dev)
-            ms32, st32, bsa32 = time_layer(L32, q32, k32, v32, p32, args.steps, args.warmup, torch)
-            f32_ = 4 * p32.d * visible_pairs(p32, L32.mask.cpu().numpy().view(np.uint32), L32.NB)
-            out["l32k"] = {"ms_per_layer": round(ms32, 4), "tflops": round(f32_ / (ms32 * 1e-3) / 1e12, 2),
-                           "bsa_ms": round(float(np.mean(bsa32)), 4),
-                           "bsa_tflops": round(f32_ / (float(np.mean(bsa32)) * 1e-3) / 1e12, 2)}
-            del L32, q32, k32, v32
+        if args.workload == "llama_128k_bf16" and not args.no_other_workloads:
+            others = {}
+            for name in ("llama_32k_bf16", "w8a8_128k_fp8", "paged_ragged_bf16", "tiny_f32"):
+                log(f"[bench] other workload {name}")
+                others[name] = measure_other(name, args.steps, args.warmup, dev, torch)
+                torch.cuda.empty_cache()
+            out["other_workloads"] = others
     if args.copy_calibration:
         buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(buf)
