@@ -126,6 +126,77 @@ def measure_other(name, steps, warmup, dev, torch):
             "peak_tflops": peak}
 
 
+def unpack_bits(p, words, r, NB_off):
+    """Request r's selection as bool [hq][n][n] (causal part only) from packed mask words."""
+    n = p.nblocks(r)
+    w = words[:, NB_off:NB_off + n].astype(np.uint32)
+    bits = ((w[..., None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(p.hq, n, -1)[:, :, :n].astype(bool)
+    return bits & np.tril(np.ones((n, n), dtype=bool))[None]
+
+
+def selection_stats(p, words, ref_words):
+    """Where a selection puts its blocks, and how much of it a reference selection shares."""
+    cb = p.cu_blocks
+    inter = union = total = sink = diag = local = 0
+    dist = 0.0
+    for r in range(len(p.lens)):
+        n = p.nblocks(r)
+        a = unpack_bits(p, words, r, cb[r])
+        b = unpack_bits(p, ref_words, r, cb[r])
+        inter += int((a & b).sum())
+        union += int((a | b).sum())
+        ii, jj = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+        total += int(a.sum())
+        sink += int(a[:, :, 0].sum())
+        diag += int(a[:, ii == jj].sum())
+        local += int(a[:, (ii - jj < 16)].sum())
+        dist += float(((ii - jj)[None] * a).sum())
+    return {"jaccard_vs_default": round(inter / max(union, 1), 4), "blocks": total,
+            "frac_sink_block": round(sink / total, 4), "frac_diagonal": round(diag / total, 4),
+            "frac_within_16_blocks": round(local / total, 4), "mean_block_distance": round(dist / total, 2)}
+
+
+def measure_ablations(L, q, k, v, p, torch, reps=3):
+    """The pages' ablation switches on the same inputs: uniform budget (mu = 1), routing only (beta = 0),
+    both, and a small beta/mu sweep.  Reports latency and where the selection goes (model accuracy needs
+    weights and is out of reach here)."""
+    rho = (p.rho_num, p.rho_den)
+
+    def run(beta, mu):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record()
+        for _ in range(reps):
+            L.score(q, k, v, beta)
+            L.select(rho, mu)
+        b.record()
+        for _ in range(reps):
+            L.attend(q, k, v, "selected", True)
+        c.record()
+        torch.cuda.synchronize()
+        words = L.mask.cpu().numpy().view(np.uint32)
+        counts = L.counts.cpu().numpy()
+        return a.elapsed_time(b) / reps, b.elapsed_time(c) / reps, words, counts
+
+    sel_ms, bsa_ms, ref, _ = run(p.beta, (p.mu_num, p.mu_den))
+    res = {}
+    variants = [("default", p.beta, (p.mu_num, p.mu_den)), ("uniform_mu1", p.beta, (1, 1)),
+                ("routing_only_beta0", 0.0, (p.mu_num, p.mu_den)), ("uniform_and_beta0", 0.0, (1, 1))]
+    variants += [(f"beta{b}_mu{m[0]}/{m[1]}", b, m) for b in (0.1, 0.4, 0.8) for m in ((1, 2), (7, 10))]
+    n_last = p.nblocks(len(p.lens) - 1)
+    for name, beta, mu in variants:
+        sel_ms, bsa_ms, words, counts = run(beta, mu)
+        fl = 4 * p.d * visible_pairs(p, words, L.NB)
+        last = counts[0, p.cu_blocks[-2]:p.cu_blocks[-1]]
+        res[name] = {"beta": beta, "mu": f"{mu[0]}/{mu[1]}", "score_select_ms": round(sel_ms, 4),
+                     "bsa_ms": round(bsa_ms, 3), "bsa_tflops": round(fl / (bsa_ms * 1e-3) / 1e12, 2),
+                     "k_first_uncapped_row": int(last[np.argmax(last < np.arange(1, n_last + 1))]),
+                     "k_last_row": int(last[-1]), **selection_stats(p, words, ref)}
+    L.score(q, k, v, p.beta)
+    L.select(rho, (p.mu_num, p.mu_den))
+    torch.cuda.synchronize()
+    return res
+
+
 def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
     """The oracle, as it stands, on a bounded sample of rows of the same workload: for each sampled
     (query head, query block) row it pools, scores, takes the TPD budget, selects and attends.
@@ -199,6 +270,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense run, the density sweep and the other workloads")
     ap.add_argument("--no-other-workloads", action="store_true", help="skip the 32K / fp8 / paged / fp32 lines")
+    ap.add_argument("--no-ablations", action="store_true", help="skip the mu = 1 / beta = 0 ablation switches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -274,6 +346,9 @@ def main():
                                "density": round(f2 / (4 * p.d * dense_pairs(p)), 4)}
         out["density_sweep"] = sweep
         L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
+        if not args.no_ablations:
+            log("[bench] ablation switches (mu = 1, beta = 0, beta/mu sweep)")
+            out["ablations"] = measure_ablations(L, q, k, v, p, torch)
         if args.workload == "llama_128k_bf16" and not args.no_other_workloads:
             others = {}
             for name in ("llama_32k_bf16", "w8a8_128k_fp8", "paged_ragged_bf16", "tiny_f32"):

@@ -105,6 +105,8 @@ SMALL = [
     ("llama_32k_bf16", dict(lens=(777,), hq=8, hkv=1, d=64)),
     ("llama_32k_bf16", dict(lens=(640,), hq=4, hkv=2, block=64)),
     ("llama_32k_bf16", dict(lens=(1500,), hq=4, hkv=1, rho_num=50, mu_num=1, mu_den=1)),
+    ("llama_32k_bf16", dict(lens=(1100, 2000), hq=8, hkv=2, beta=0.0)),
+    ("llama_32k_bf16", dict(lens=(3000,), hq=4, hkv=1, beta=0.0, mu_num=1, mu_den=1)),
     ("w8a8_128k_fp8", dict(lens=(1000,), hq=8, hkv=2)),
     ("w8a8_128k_fp8", dict(lens=(200, 513), hq=4, hkv=1, d=64)),
     ("paged_ragged_bf16", dict(lens=(300, 64, 700), hq=4, hkv=2)),
@@ -132,7 +134,7 @@ def test_small_case_all_outputs(dev, name, over):
     assert lerr <= 10 * tmax
 
 
-@pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[7], SMALL[9]],
+@pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[9], SMALL[11]],
                          ids=["f32", "bf16", "fp8", "paged"])
 def test_dense_mode_matches_textbook_attention(dev, name, over):
     """mask = NULL runs dense causal attention: the 100%-budget special case of the oracle."""
@@ -221,6 +223,38 @@ def test_full_size_workload(dev, name):
     mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
     _log(f"[full] {name}: score rel {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, "
          f"lse {lerr:.2e}")
+    tmax, tmean = sc.TOL[p.dtype]
+    assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+
+
+# ------------------------------------------------------------------------------------ ablation switches
+ABLATIONS = [dict(mu_num=1, mu_den=1), dict(beta=0.0), dict(beta=0.0, mu_num=1, mu_den=1),
+             dict(beta=0.8, mu_num=1, mu_den=2)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("over", ABLATIONS, ids=["uniform_mu1", "beta0", "uniform_beta0", "beta0.8_mu0.5"])
+def test_ablation_switches_full_size_32k(dev, over):
+    """The pages' ablations (uniform budget, routing-only score) at the 32K workload: every budget and
+    selection against the oracle, attention on sampled rows."""
+    p = synth.make_problem("llama_32k_bf16", **over)
+    _log(f"[ablation] {over}")
+    x = synth.make_inputs(p, seed=0)
+    ref1 = sc.oracle_stage1(p, x)
+    S_list = [s for *_, s in ref1]
+    budgets = sc.oracle_budgets(p)
+    if p.mu_num == p.mu_den:
+        b = budgets[0]
+        uncapped = b < np.arange(1, len(b) + 1)
+        assert np.ptp(b[uncapped]) <= 1  # uniform: every uncapped row gets the same budget up to rounding
+    masks = sc.oracle_masks(S_list, budgets)
+    g = _run(p, x, dev, masks_for_bsa=masks)
+    worst = _check_stage1(p, g, ref1)
+    ties = sc.check_selection(p, S_list, budgets, g["words"], g["counts"])
+    rows = [sc.sample_rows(p, 0, 8)]
+    ora = sc.oracle_attention(p, x, masks, rows)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
+    _log(f"  score rel {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
     tmax, tmean = sc.TOL[p.dtype]
     assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
 
