@@ -18,13 +18,17 @@
 //  * S^T = K Q^T (v_mfma_f32_32x32x16_bf16): K operand = one ds_read_b128 per MFMA.  O^T = V^T P^T: the V^T
 //    operand is gathered from the row-major V tile by two ds_read_b64_tr_b16 (transposing 16-bit reads),
 //    in the key order that the S^T accumulator layout gives P^T, so P never moves between lanes.
-//  * softmax: raw v_exp_f32 (no denormal fix-up), one FMA folds the scale and the running max, the row
-//    max is one v_permlane32_swap away, and the O^T rescale is lazy: the reference max is only raised
-//    when a tile's max exceeds it by more than 2^8 (exact arithmetic with a different reference point;
-//    p <= 256 fits bf16), so after the first blocks the rescale is skipped.
-//  * per-thread global offsets are computed once; each sub-tile only changes a uniform base address
-//    (contiguous K/V, or pages of >= 64 tokens); small pages look up one page per row.  The diagonal block
-//    takes a separate path with the causal mask; other blocks have no per-element compares.
+//  * softmax: raw v_exp_f32 (no denormal fix-up) of one FMA that folds the scale and the reference max.
+//    There is no per-tile row max: the reference is taken from the first visible keys of each row and
+//    kept while a tile's sum of P stays <= 2^32 (bf16 and fp32 have the same exponent range, so P keeps
+//    its relative precision at any scale); a larger sum (or inf) recomputes the tile's scores, moves
+//    the reference to their max and rescales O^T and the sum exactly.  The row sum adds the rounded P
+//    pairs with v_dot2_f32_bf16 (the same values PV multiplies).
+//  * sub-tile loads are buffer loads (contiguous K/V, or pages of >= 64 tokens): the sub-tile's base
+//    address is scalar and each lane's byte offset is fixed, so issuing a load costs no vector
+//    instructions; rows past the request's end fall outside the buffer and read as zeros.  Small pages
+//    look up one page per row.  The diagonal block takes a separate path with the causal mask; other
+//    blocks have no per-element compares.
 #include "stem_internal.h"
 
 namespace stem {
@@ -37,7 +41,14 @@ constexpr int KT = 64;
 constexpr int NT = 256;
 constexpr int TILE = KT * D * 2;  // bytes per K or V sub-tile
 constexpr int kMaxList = 2048;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
+// Softmax reference point: the reference max m_run (log2 units) is set from the first visible keys of a
+// row and then kept while the tile sums of P = 2^(s - m_run) stay <= 2^32 (no overflow anywhere in P,
+// the row sum or O^T); a larger sum rebases to the tile's max.  P keeps bf16's relative precision at any
+// scale, so no per-tile max is needed.
+constexpr float kNoReference = -1e29f;
+constexpr float kOverflow = 4294967296.0f;
+// Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts.
+constexpr int kBufDword3 = 0x00020000;
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -140,8 +151,12 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
 
   // ---- loader geometry: instruction m of this wave fills LDS chunk (4*wave + m) = tile rows
   //      16*wave + 4*m + lane/16, slot lane & 15 (16 bytes); the lane fetches the swizzled source chunk.
+  //      Contiguous K/V and pages of >= 64 tokens: buffer loads whose base (the sub-tile's first row) is
+  //      scalar and whose per-lane byte offsets never change, with the buffer size ending at the
+  //      request's last row (rows past it read as zeros; they are causally masked).  Smaller pages: one
+  //      page lookup per row and global addresses.
   const int64_t row_stride = (int64_t)a.hkv * D * 2;
-  int ldrow[4], kchunk[4], vchunk[4];
+  int ldrow[4], kchunk[4], vchunk[4], koff_ld[4], voff_ld[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int row = 16 * wave + 4 * m + (lane >> 4);
@@ -149,6 +164,8 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     ldrow[m] = row;
     kchunk[m] = slot ^ (row & 15);
     vchunk[m] = slot ^ (4 * (row & 3));
+    koff_ld[m] = row * (int)row_stride + kchunk[m] * 16;
+    voff_ld[m] = row * (int)row_stride + vchunk[m] * 16;
   }
   const uint8_t* kbase_all = (const uint8_t*)a.k;
   const uint8_t* vbase_all = (const uint8_t*)a.v;
@@ -159,40 +176,44 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     return j * B + (u & 1) * KT;
   };
 
+  // The loads of sub-tile u: part m fills LDS chunk m of this wave in K and in V.  kb/vb: the sub-tile's
+  // first row (scalar); nrec: bytes up to the request's end.
+  auto issue_part = [&](int kp0, int nrec, const uint8_t* kb, const uint8_t* vb, lds_u8* kl, lds_u8* vl, int m) {
+    if (PAGE == 0 || PAGE == 1) {
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)kb, 0, nrec, kBufDword3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, nrec, kBufDword3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kl + m * 1024, 16, koff_ld[m], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vl + m * 1024, 16, voff_ld[m], 0, 0, 0);
+    } else {
+      const int kp = min(kp0 + ldrow[m], L - 1);
+      const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp / a.kv.page_size];
+      const int64_t off = ((int64_t)page * a.kv.page_size + (kp % a.kv.page_size)) * row_stride + head_off;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase_all + off + kchunk[m] * 16), kl + m * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vbase_all + off + vchunk[m] * 16), vl + m * 1024, 16, 0, 0);
+    }
+  };
+  // Scalar base of sub-tile u (contiguous K/V or one page of >= 64 tokens).
+  auto tile_base = [&](int kp0) -> int64_t {
+    int64_t tok0;  // token index (pool row) of the sub-tile's first key
+    if (PAGE == 0) {
+      tok0 = (int64_t)tb + kp0;
+    } else if (PAGE == 1) {
+      const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp0 / a.kv.page_size];
+      tok0 = (int64_t)page * a.kv.page_size + (kp0 % a.kv.page_size);
+    } else {
+      tok0 = 0;
+    }
+    return tok0 * row_stride + head_off;
+  };
   auto issue_loads = [&](int u, uint8_t* kdst, uint8_t* vdst) {
     const int kp0 = sub_key0(u);
     if (kp0 >= L) return;  // a second half-block past the end of the request: nothing to load
-    lds_u8* kl = (lds_u8*)kdst + wave * 4096;
-    lds_u8* vl = (lds_u8*)vdst + wave * 4096;
-    const bool full = kp0 + KT <= L;
-    if (PAGE == 0 || PAGE == 1) {
-      int64_t tok0;  // token index (pool row) of the sub-tile's first key
-      if (PAGE == 0) {
-        tok0 = (int64_t)tb + kp0;
-      } else {
-        const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp0 / a.kv.page_size];
-        tok0 = (int64_t)page * a.kv.page_size + (kp0 % a.kv.page_size);
-      }
-      const int64_t base = tok0 * row_stride + head_off;
+    const int64_t base = tile_base(kp0);
+    const int nrec = min(L - kp0, KT) * (int)row_stride;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        int row = ldrow[m];
-        if (!full) row = min(row, L - 1 - kp0);  // keys past the end repeat the last key (masked anyway)
-        const int64_t off = base + (int64_t)row * row_stride;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase_all + off + kchunk[m] * 16), kl + m * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase_all + off + vchunk[m] * 16), vl + m * 1024, 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int kp = min(kp0 + ldrow[m], L - 1);
-        const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp / a.kv.page_size];
-        const int64_t off =
-            ((int64_t)page * a.kv.page_size + (kp % a.kv.page_size)) * row_stride + head_off;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase_all + off + kchunk[m] * 16), kl + m * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase_all + off + vchunk[m] * 16), vl + m * 1024, 16, 0, 0);
-      }
-    }
+    for (int m = 0; m < 4; ++m)
+      issue_part(kp0, nrec, kbase_all + base, vbase_all + base, (lds_u8*)kdst + wave * 4096,
+                 (lds_u8*)vdst + wave * 4096, m);
   };
 
   // ---- operand read offsets (bytes inside a tile)
@@ -228,45 +249,58 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     __syncthreads();
     if (u + 1 < nsub) issue_loads(u + 1, knext, vnext);
     const int kp0 = sub_key0(u);
-    if (kp0 >= L) return;
     const bool diag = (kp0 / B) == i;
-    if (diag && kp0 > i * B + wave * 32 + 31) return;  // every key of this sub-tile is after the wave's rows
+    // nothing to compute: the sub-tile starts past the request's end, or (diagonal block) every key is
+    // after the wave's rows
+    const bool idle = kp0 >= L || (diag && kp0 > i * B + wave * 32 + 31);
+    if (idle) return;
     const lds_u8* Kt = (const lds_u8*)kcur;
     const lds_u8* Vt = (const lds_u8*)vcur;
     f32x16 s0, s1;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      s0[x] = 0.f;
-      s1[x] = 0.f;
-    }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint32_t off = koffs[kk];
-      const bf16x8 a0 = *(const __attribute__((address_space(3))) bf16x8*)(Kt + off);
-      const bf16x8 a1 = *(const __attribute__((address_space(3))) bf16x8*)(Kt + off + 32 * 256);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
-    }
-    if (diag) {
+    auto scores = [&]() {
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int kl = 8 * (x >> 2) + 4 * half + (x & 3);
-        if (kp0 + kl > qpos) s0[x] = -INFINITY;
-        if (kp0 + 32 + kl > qpos) s1[x] = -INFINITY;
+        s0[x] = 0.f;
+        s1[x] = 0.f;
       }
-    }
-    float mx = max3(s0[0], s0[1], s1[0]);
-    mx = max3(mx, s0[2], s1[1]);
+      // K fragments are read two k-steps ahead of the MFMAs that use them (hides the LDS latency)
+      bf16x8 ka[3], kb[3];
 #pragma unroll
-    for (int x = 3; x < 16; ++x) mx = max3(mx, s0[x], s1[x - 1]);
-    mx = fmaxf(mx, s1[15]);
-    {
+      for (int kk = 0; kk < 2; ++kk) {
+        ka[kk] = *(const __attribute__((address_space(3))) bf16x8*)(Kt + koffs[kk]);
+        kb[kk] = *(const __attribute__((address_space(3))) bf16x8*)(Kt + koffs[kk] + 32 * 256);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 2 < 8) {
+          ka[(kk + 2) % 3] = *(const __attribute__((address_space(3))) bf16x8*)(Kt + koffs[kk + 2]);
+          kb[(kk + 2) % 3] = *(const __attribute__((address_space(3))) bf16x8*)(Kt + koffs[kk + 2] + 32 * 256);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3], qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3], qf[kk], s1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (diag) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int kl = 8 * (x >> 2) + 4 * half + (x & 3);
+          if (kp0 + kl > qpos) s0[x] = -INFINITY;
+          if (kp0 + 32 + kl > qpos) s1[x] = -INFINITY;
+        }
+      }
+    };
+    // Move the reference max to this tile's max (the O^T, sum rescale by 2^(old - new) is exact).
+    auto rebase = [&]() {
+      float mx = max3(s0[0], s0[1], s1[0]);
+      mx = max3(mx, s0[2], s1[1]);
+#pragma unroll
+      for (int x = 3; x < 16; ++x) mx = max3(mx, s0[x], s1[x - 1]);
+      mx = fmaxf(mx, s1[15]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mt = mx * c2;
-    if (__ballot(mt > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mt);
+      const float m_new = fmaxf(m_run, mx * c2);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
@@ -274,24 +308,45 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) o[dt][x] *= alpha;
       m_run = m_new;
-    }
-    const float negm = -m_run;
-    float ps = 0.f;
+    };
+    uint4 pw[4];  // P rounded to bf16 pairs, the B operand of each k-step
+    // P = 2^(s c2 - m_run), packed; returns the sum of the rounded values (v_dot2_f32_bf16 with (1, 1)).
+    auto exp_pack = [&]() -> float {
+      const float negm = -m_run;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
-      s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
-      ps += s0[x] + s1[x];
+      for (int x = 0; x < 16; ++x) {
+        s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
+        s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
+      }
+      const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const f32x16& st = (mm < 2) ? s0 : s1;
+        const int x0 = 8 * (mm & 1);
+        pw[mm] = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
+                            cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].x), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].y), ones, ps1, false);
+        ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].z), ones, ps0, false);
+        ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].w), ones, ps1, false);
+      }
+      return ps0 + ps1;
+    };
+
+    // Rebase at the first visible keys of a row; if a tile overflows the reference, compute it again
+    // with a rebase (at most once: after a rebase every P is <= 1).
+    bool force = __ballot(m_run < kNoReference) != 0;
+    float ps;
+    for (;;) {
+      asm volatile("" ::: "memory");  // keep the K reads inside the (rarely repeated) loop body
+      scores();
+      if (force) rebase();
+      ps = exp_pack();
+      if (force || __ballot(!(ps <= kOverflow)) == 0) break;
+      force = true;
     }
     l_part += ps;
-    uint4 pw[4];  // P rounded to bf16 pairs, the B operand of each k-step
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const f32x16& st = (mm < 2) ? s0 : s1;
-      const int x0 = 8 * (mm & 1);
-      pw[mm] = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
-                          cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
-    }
 
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
