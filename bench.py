@@ -97,13 +97,13 @@ def time_layer(L, q, k, v, p, steps, warmup, torch):
     return wall, stage.mean(axis=0), stage[:, 2]
 
 
-def time_bsa(L, q, k, v, mask, reps, torch):
-    L.attend(q, k, v, mask, False)
+def time_bsa(L, q, k, v, mask, reps, torch, inloop=False):
+    L.attend(q, k, v, mask, False, inloop=inloop)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        L.attend(q, k, v, mask, False)
+        L.attend(q, k, v, mask, False, inloop=inloop)
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
@@ -344,6 +344,11 @@ def main():
             t2 = time_bsa(L, q, k, v, L.mask, 3, torch)
             sweep[f"{rn}%"] = {"bsa_ms": round(t2, 3), "tflops": round(f2 / (t2 * 1e-3) / 1e12, 2),
                                "density": round(f2 / (4 * p.d * dense_pairs(p)), 4)}
+            if p.dtype == "bf16" and p.d == 128 and p.block == 128 and not p.paged:
+                # the same mask through the variant that tests each block's bit inside the loop
+                t3 = time_bsa(L, q, k, v, L.mask, 3, torch, inloop=True)
+                sweep[f"{rn}%"]["inloop_skip_ms"] = round(t3, 3)
+                sweep[f"{rn}%"]["list_speedup_over_inloop"] = round(t3 / t2, 4)
         out["density_sweep"] = sweep
         L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
         if not args.no_ablations:

@@ -25,7 +25,8 @@ DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 MAX_REQS = 256
 
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
-           "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill"]
+           "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
+           "bsa_prefill_inloop"]
 
 
 class StemError(RuntimeError):
@@ -79,8 +80,9 @@ def lib() -> ctypes.CDLL:
         L.stem_score.argtypes = [P, vp, vp, vp, ctypes.c_float, vp, i64, vp, sz, vp]
         L.stem_tpd_topk.argtypes = [P, vp, i64, i32, i32, i32, i32, vp, i32, vp, vp]
         L.bsa_prefill.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
+        L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         for name in ("stem_block_counts", "stem_workspace_layout", "stem_tpd_budgets_host", "stem_score",
-                     "stem_tpd_topk", "bsa_prefill"):
+                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,3 +191,10 @@ def bsa_prefill(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float =
     words = int(mask.shape[-1]) if mask is not None else 0
     _check(lib().bsa_prefill(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), words, float(softmax_scale),
                              _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def bsa_prefill_inloop(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float = 0.0, stream=None) -> None:
+    """The comparison variant with the skip test inside the loop (same outputs as bsa_prefill)."""
+    words = int(mask.shape[-1]) if mask is not None else 0
+    _check(lib().bsa_prefill_inloop(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), words, float(softmax_scale),
+                                    _ptr(out), _ptr(lse), _stream(stream)))

@@ -65,11 +65,16 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 }
 
 // PAGE: 0 contiguous K/V, 1 pages of a multiple of 64 tokens (one page per sub-tile), 2 smaller pages.
-template <int PAGE, bool MASKED>
+// INLOOP (with MASKED): the comparison variant that keeps the skip decision inside the loop: no list; the
+// loop walks every causal block j <= i and tests j's mask bit (kept in LDS) at each step, skipping the
+// compute and the loads of unselected blocks but not the step itself (its barrier and bookkeeping).
+// Selected blocks see exactly the same arithmetic in the same order, so the outputs are identical.
+template <int PAGE, bool MASKED, bool INLOOP = false>
 __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   // Two buffers, each its own LDS object, so the loads into one are known not to alias reads of the other.
   __shared__ __align__(1024) uint8_t kbuf0[TILE], vbuf0[TILE], kbuf1[TILE], vbuf1[TILE];
-  __shared__ uint16_t list[MASKED ? kMaxList : 1];
+  __shared__ uint16_t list[(MASKED && !INLOOP) ? kMaxList : 1];
+  __shared__ uint32_t mbits[INLOOP ? kMaxList / 32 : 1];
   __shared__ int list_len;
 
   const int tid = threadIdx.x;
@@ -97,7 +102,15 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
 
   // ---- list of selected blocks
   int nsel;
-  if constexpr (MASKED) {
+  if constexpr (INLOOP) {
+    if (wave == 0) {
+      const uint32_t* mrow = a.mask + ((int64_t)h * a.NB + ib) * a.mask_words;
+      const int nwords = (i >> 5) + 1;
+      for (int w = lane; w < nwords; w += 64) mbits[w] = mrow[w];
+    }
+    __syncthreads();
+    nsel = i + 1;
+  } else if constexpr (MASKED) {
     if (wave == 0) {
       const uint32_t* mrow = a.mask + ((int64_t)h * a.NB + ib) * a.mask_words;
       const int nwords = (i >> 5) + 1;
@@ -172,8 +185,17 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   const int64_t head_off = (int64_t)g * D * 2;
 
   auto sub_key0 = [&](int u) -> int {
-    const int j = MASKED ? (int)list[u >> 1] : (u >> 1);
+    const int j = (MASKED && !INLOOP) ? (int)list[u >> 1] : (u >> 1);
     return j * B + (u & 1) * KT;
+  };
+  // in-loop variant: is sub-tile u's block selected?
+  auto selected = [&](int u) -> bool {
+    if constexpr (INLOOP) {
+      const int j = u >> 1;
+      return (mbits[j >> 5] >> (j & 31)) & 1u;
+    } else {
+      return true;
+    }
   };
 
   // The loads of sub-tile u: part m fills LDS chunk m of this wave in K and in V.  kb/vb: the sub-tile's
@@ -247,12 +269,12 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   auto step = [&](int u, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (u + 1 < nsub) issue_loads(u + 1, knext, vnext);
+    if (u + 1 < nsub && selected(u + 1)) issue_loads(u + 1, knext, vnext);
     const int kp0 = sub_key0(u);
     const bool diag = (kp0 / B) == i;
     // nothing to compute: the sub-tile starts past the request's end, or (diagonal block) every key is
-    // after the wave's rows
-    const bool idle = kp0 >= L || (diag && kp0 > i * B + wave * 32 + 31);
+    // after the wave's rows, or (in-loop variant) its block is not selected
+    const bool idle = kp0 >= L || (diag && kp0 > i * B + wave * 32 + 31) || !selected(u);
     if (idle) return;
     const lds_u8* Kt = (const lds_u8*)kcur;
     const lds_u8* Vt = (const lds_u8*)vcur;
@@ -364,7 +386,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     }
   };
 
-  if (nsub > 0) issue_loads(0, kbuf0, vbuf0);
+  if (nsub > 0 && selected(0)) issue_loads(0, kbuf0, vbuf0);
   for (int u = 0; u < nsub; u += 2) {
     step(u, kbuf0, vbuf0, kbuf1, vbuf1);
     if (u + 1 < nsub) step(u + 1, kbuf1, vbuf1, kbuf0, vbuf0);
@@ -408,6 +430,13 @@ hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s) {
   else if (page_mode == 1) STEM_LAUNCH(1);
   else STEM_LAUNCH(2);
 #undef STEM_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_bsa_bf16_inloop(const BsaArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)(a.hq * a.NB));
+  dim3 block(NT);
+  hipLaunchKernelGGL((bsa_bf16_kernel<0, true, true>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

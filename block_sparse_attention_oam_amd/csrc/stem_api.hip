@@ -312,44 +312,65 @@ int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_
   return hip_status(launch_topk(ta, pl.max_n, p->num_reqs, (hipStream_t)stream), "topk launch");
 }
 
-int bsa_prefill(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
-                int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream) {
-  Plan pl;
-  int st = make_plan(p, &pl);
+static int prepare_bsa(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
+                       int32_t mask_row_words, float softmax_scale, void* out, float* lse, Plan* pl, BsaArgs* ba) {
+  int st = make_plan(p, pl);
   if (st != STEM_OK) return st;
   if (!q || !k || !v || !out) return fail(STEM_E_INVALID_ARG, "q, k, v and out must be non-NULL");
-  if (mask && mask_row_words < (pl.max_n + 31) / 32)
-    return fail(STEM_E_INVALID_ARG, "mask_row_words = %d < %d", mask_row_words, (pl.max_n + 31) / 32);
-  if (mask && pl.max_n > 2048) return fail(STEM_E_UNSUPPORTED, "masked attention supports up to 2048 blocks per request");
+  if (mask && mask_row_words < (pl->max_n + 31) / 32)
+    return fail(STEM_E_INVALID_ARG, "mask_row_words = %d < %d", mask_row_words, (pl->max_n + 31) / 32);
+  if (mask && pl->max_n > 2048) return fail(STEM_E_UNSUPPORTED, "masked attention supports up to 2048 blocks per request");
   if (!isfinite(softmax_scale)) return fail(STEM_E_INVALID_ARG, "softmax_scale is not finite");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15)
     return fail(STEM_E_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  ba->q = q;
+  ba->k = k;
+  ba->v = v;
+  ba->mask = mask;
+  ba->mask_words = mask ? mask_row_words : 0;
+  ba->out = out;
+  ba->lse = lse;
+  ba->q_scale = p->q_scale;
+  ba->k_scale = p->k_scale;
+  ba->v_scale = p->v_scale;
+  ba->hq = p->hq;
+  ba->hkv = p->hkv;
+  ba->B = p->block;
+  ba->NB = pl->NB;
+  ba->tokens = pl->tokens;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)p->head_dim);
+  ba->scale = sc;
+  ba->scale_log2 = sc * 1.44269504088896340736f;
+  ba->xcd_remap = ((int64_t)p->hq * pl->NB) % 8 == 0 ? 1 : 0;
+  ba->kv = pl->kv;
+  ba->rt = pl->rt;
+  return STEM_OK;
+}
+
+int bsa_prefill(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
+                int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream) {
+  Plan pl;
+  BsaArgs ba;
+  int st = prepare_bsa(p, q, k, v, mask, mask_row_words, softmax_scale, out, lse, &pl, &ba);
+  if (st != STEM_OK) return st;
   st = check_device();
   if (st != STEM_OK) return st;
-  BsaArgs ba;
-  ba.q = q;
-  ba.k = k;
-  ba.v = v;
-  ba.mask = mask;
-  ba.mask_words = mask ? mask_row_words : 0;
-  ba.out = out;
-  ba.lse = lse;
-  ba.q_scale = p->q_scale;
-  ba.k_scale = p->k_scale;
-  ba.v_scale = p->v_scale;
-  ba.hq = p->hq;
-  ba.hkv = p->hkv;
-  ba.B = p->block;
-  ba.NB = pl.NB;
-  ba.tokens = pl.tokens;
-  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)p->head_dim);
-  ba.scale = sc;
-  ba.scale_log2 = sc * 1.44269504088896340736f;
-  ba.xcd_remap = ((int64_t)p->hq * pl.NB) % 8 == 0 ? 1 : 0;
-  ba.kv = pl.kv;
-  ba.rt = pl.rt;
   return hip_status(launch_bsa(ba, p->dtype, p->head_dim, p->kv_paged != 0, mask != nullptr, (hipStream_t)stream),
                     "bsa launch");
+}
+
+int bsa_prefill_inloop(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
+                       int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream) {
+  Plan pl;
+  BsaArgs ba;
+  if (!mask) return fail(STEM_E_INVALID_ARG, "the in-loop skip variant needs a mask");
+  int st = prepare_bsa(p, q, k, v, mask, mask_row_words, softmax_scale, out, lse, &pl, &ba);
+  if (st != STEM_OK) return st;
+  if (!bsa_bf16_supported(p->dtype, p->head_dim, p->block) || p->kv_paged)
+    return fail(STEM_E_UNSUPPORTED, "the in-loop skip variant supports bf16, head_dim 128, block 128, contiguous K/V");
+  st = check_device();
+  if (st != STEM_OK) return st;
+  return hip_status(launch_bsa_bf16_inloop(ba, (hipStream_t)stream), "bsa in-loop launch");
 }
 
 }  // extern "C"

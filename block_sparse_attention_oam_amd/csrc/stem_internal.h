@@ -87,6 +87,7 @@ hipError_t launch_topk(const TopkArgs& a, int max_n, int num_reqs, hipStream_t s
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int head_dim, bool paged, bool masked, hipStream_t s);
 bool bsa_bf16_supported(int dtype, int head_dim, int block);
 hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s);
+hipError_t launch_bsa_bf16_inloop(const BsaArgs& a, hipStream_t s);
 bool bsa_fp8_supported(int dtype, int head_dim, int block);
 hipError_t launch_bsa_fp8(const BsaArgs& a, bool masked, hipStream_t s);
 

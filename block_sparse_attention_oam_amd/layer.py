@@ -53,9 +53,11 @@ class StemPrefill:
     def select(self, rho=(25, 100), mu=(7, 10), stream=None):
         _abi.stem_tpd_topk(self.p, self.scores, rho, mu, self.mask, self.counts, stream)
 
-    def attend(self, q, k, v, mask="selected", lse=True, softmax_scale=0.0, stream=None):
+    def attend(self, q, k, v, mask="selected", lse=True, softmax_scale=0.0, stream=None, inloop=False):
+        """inloop=True runs the comparison variant that tests the mask inside the loop."""
         m = self.mask if isinstance(mask, str) and mask == "selected" else mask
-        _abi.bsa_prefill(self.p, q, k, v, m, self.out, self.lse if lse else None, softmax_scale, stream)
+        fn = _abi.bsa_prefill_inloop if inloop else _abi.bsa_prefill
+        fn(self.p, q, k, v, m, self.out, self.lse if lse else None, softmax_scale, stream)
 
     def forward(self, q, k, v, beta=0.2, rho=(25, 100), mu=(7, 10), stream=None):
         self.score(q, k, v, beta, stream)

@@ -95,7 +95,7 @@ size_t stem_workspace_bytes(const stem_problem* p);
 int stem_workspace_layout(const stem_problem* p, size_t* off_qbar, size_t* off_kbar, size_t* off_m);
 
 /* TPD budgets of one request with n blocks, written to HOST k_out[n] (same arithmetic as the kernel).
- * Budget fraction rho = rho_num/rho_den in [0, 1]; decay ratio mu = mu_num/mu_den in [0, 1].
+ * Budget fraction rho = rho_num/rho_den in [0, 1]; decay ratio mu = mu_num/mu_den in (0, 1].
  * Total T = round-half-up(rho * n(n+1)/2) clamped to [n, n(n+1)/2].  Row i (0-based) has the linear
  * weight w_i = 1 - (1 - mu) i/(n-1); its real budget is r_i = min(max(x w_i, 1), i+1) with x solving
  * sum r_i = T; integer budgets round the prefix sums: k_i = floor(P_i + 1/2) - floor(P_{i-1} + 1/2).
@@ -133,6 +133,17 @@ int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_
  * v_scale[g]. */
 int bsa_prefill(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
                 int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream);
+
+/* Comparison variant of bsa_prefill with the skip decision inside the loop: instead of building each
+ * row's list of selected blocks, it walks every causal block j <= i and tests j's mask bit at each step,
+ * skipping the loads and the compute of unselected blocks but not the step.  Same arguments and same
+ * outputs as bsa_prefill (bit for bit: the selected blocks see the same arithmetic in the same order);
+ * it exists to measure what building the list saves.  mask must be non-NULL; only bf16, head_dim 128,
+ * block 128 and contiguous K/V are supported (STEM_E_UNSUPPORTED otherwise).
+ * Source: "HPC-BSA：跳块零开销的秘密" (a skip test inside the inner loop costs divergence and pipeline
+ * bubbles; the list moves the decision out of the loop). */
+int bsa_prefill_inloop(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
+                       int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -140,6 +140,7 @@ def test_invalid_problem_is_rejected_by_every_entry_point(kw, msg):
         lambda: stem.stem_score(p, T(), T(), T(), 0.2, T(shape=(1, 1, 64)), T(shape=(1 << 30,), elem=1), stream=0),
         lambda: stem.stem_tpd_topk(p, T(shape=(1, 1, 64)), (1, 4), (7, 10), T(shape=(1, 1, 2)), T(), stream=0),
         lambda: stem.bsa_prefill(p, T(), T(), T(), None, T(), stream=0),
+        lambda: _abi.bsa_prefill_inloop(p, T(), T(), T(), T(shape=(8, 24, 1)), T(), stream=0),
     ]
     for c in calls:
         with pytest.raises(stem.StemError) as e:
@@ -190,6 +191,28 @@ def test_call_argument_errors():
         with pytest.raises(stem.StemError) as e:
             c()
         assert msg in str(e.value), str(e.value)
+
+
+def test_inloop_variant_argument_errors():
+    """The in-loop skip comparison variant validates like bsa_prefill, needs a mask and supports only the
+    main production shape."""
+    from block_sparse_attention_oam_amd import _abi as A
+
+    T = _FakeTensor
+    p = _prob()
+    with pytest.raises(stem.StemError) as e:
+        A.bsa_prefill_inloop(p, T(), T(), T(), None, T(), stream=0)
+    assert "needs a mask" in str(e.value)
+    with pytest.raises(stem.StemError) as e:
+        A.bsa_prefill_inloop(p, T(), T(), T(), T(shape=(8, 24, 0)), T(), stream=0)
+    assert "mask_row_words" in str(e.value)
+    for kw in (dict(dtype="f32"), dict(head_dim=64), dict(block=64),
+               dict(dtype="fp8", q_scale=T(), k_scale=T(), v_scale=T())):
+        q = _prob(**kw)
+        nb, mx = stem.block_counts(q)
+        with pytest.raises(stem.StemError) as e:
+            A.bsa_prefill_inloop(q, T(), T(), T(), T(shape=(8, nb, (mx + 31) // 32)), T(), stream=0)
+        assert e.value.status == A.STEM_E_UNSUPPORTED, (kw, str(e.value))
 
 
 def test_last_error_is_cleared_by_a_successful_call():

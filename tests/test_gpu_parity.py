@@ -227,6 +227,70 @@ def test_full_size_workload(dev, name):
     assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
 
 
+# ------------------------------------------------------------------------------------ in-loop skip variant
+def _inloop_vs_list(p, x, dev, mask_dev=None):
+    """Run bsa_prefill and bsa_prefill_inloop on the same mask (the GPU's own selection by default);
+    return (list out, list lse, in-loop out, in-loop lse) as device tensors."""
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+    import block_sparse_attention_oam_amd as stem
+
+    prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype)
+    k, v, q = upload(x["k"]), upload(x["v"]), upload(x["q"])
+    L = StemPrefill(prob, dev)
+    L.score(q, k, v, p.beta)
+    L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
+    m = L.mask if mask_dev is None else mask_dev
+    L.attend(q, k, v, m)
+    o1, l1 = L.out.clone(), L.lse.clone()
+    L.out.fill_(7.0)
+    L.lse.fill_(7.0)
+    L.attend(q, k, v, m, inloop=True)
+    torch.cuda.synchronize()
+    return L, o1, l1, L.out.clone(), L.lse.clone()
+
+
+@pytest.mark.parametrize("lens,hq,hkv,rho", [((1000,), 8, 2, 25), ((300, 1, 129, 700), 4, 4, 10),
+                                             ((2000,), 4, 1, 100)])
+def test_inloop_variant_equals_list_variant_and_oracle(dev, lens, hq, hkv, rho):
+    """The skip test inside the loop visits the same blocks in the same order: outputs are identical to
+    bsa_prefill's, and both match the oracle."""
+    p = synth.make_problem("llama_32k_bf16", lens=lens, hq=hq, hkv=hkv, rho_num=rho)
+    x = synth.make_inputs(p, seed=11)
+    L, o1, l1, o2, l2 = _inloop_vs_list(p, x, dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    cb = p.cu_blocks
+    words = L.mask.cpu().numpy().view(np.uint32)
+    gm = [sc.unpack_mask(words[:, cb[r]:cb[r + 1]], p.nblocks(r)) & np.tril(np.ones((p.nblocks(r),) * 2, bool))[None]
+          for r in range(len(p.lens))]
+    ora = sc.oracle_attention(p, x, gm)
+    mx, mean, lerr = sc.compare_attention(p, ora, o2.float().cpu().numpy().astype(np.float64),
+                                          l2.cpu().numpy().astype(np.float64))
+    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= 0.2
+
+
+def test_inloop_variant_external_mask_with_empty_rows(dev):
+    p = synth.make_problem("llama_32k_bf16", lens=(900, 260), hq=4, hkv=2)
+    x = synth.make_inputs(p, seed=3)
+    rng = np.random.default_rng(12)
+    NB = sum(p.nblocks(r) for r in range(len(p.lens)))
+    words = rng.integers(0, 2 ** 32, size=(p.hq, NB, 1), dtype=np.uint64).astype(np.uint32)
+    words[0] = 0          # head 0: every row empty
+    words[2] = 0xFFFFFFFF  # head 2: dense plus bits past the diagonal
+    from block_sparse_attention_oam_amd.layer import upload
+
+    _, o1, l1, o2, l2 = _inloop_vs_list(p, x, dev, upload(words.view(np.int32)))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.timeout(600)
+def test_inloop_variant_full_size_128k(dev):
+    p = synth.make_problem("llama_128k_bf16")
+    _log("[inloop] 128K: generating inputs")
+    x = synth.make_inputs(p, seed=0)
+    _, o1, l1, o2, l2 = _inloop_vs_list(p, x, dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 # ------------------------------------------------------------------------------------ ablation switches
 ABLATIONS = [dict(mu_num=1, mu_den=1), dict(beta=0.0), dict(beta=0.0, mu_num=1, mu_den=1),
              dict(beta=0.8, mu_num=1, mu_den=2)]
