@@ -329,6 +329,24 @@ def main():
                        "unit": "TFLOP/s", "frac": round(bsa_tflops / peak, 4),
                        "traffic": traffic_from_profile(sha), "avg_launch_ms": round(bsa_ms, 4)}
     if not args.no_extras:
+        log("[bench] fused scoring + selection")
+        rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
+        ref_mask = L.mask.clone()
+        L.score_select(q, k, v, p.beta, rho, mu)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(5):
+            L.score_select(q, k, v, p.beta, rho, mu)
+        ev[1].record()
+        torch.cuda.synchronize()
+        fused_ms = ev[0].elapsed_time(ev[1]) / 5
+        out["fused_score_select"] = {
+            "ms": round(fused_ms, 4), "two_stage_ms": round(float(stage_ms[0] + stage_ms[1]), 4),
+            "speedup": round(float(stage_ms[0] + stage_ms[1]) / fused_ms, 3),
+            "same_mask": bool(torch.equal(ref_mask, L.mask)),
+            "score_tensor_bytes_avoided": int(4 * sum(p.hq * p.nblocks(r) * (p.nblocks(r) + 1) for r in range(len(p.lens)))),
+        }
         log("[bench] dense-causal run of the same kernel")
         dense_ms = time_bsa(L, q, k, v, None, 3, torch)
         dflops = 4 * p.d * dense_pairs(p)

@@ -2,5 +2,6 @@
 selection and block-sparse flash attention, as a C-ABI library (libstem.so) with a thin Python binding."""
 from ._abi import (  # noqa: F401
     DTYPES, EXPORTS, LIB_PATH, Problem, StemError, block_counts, bsa_prefill, lib, make_problem,
-    stem_score, stem_tpd_budgets_host, stem_tpd_topk, workspace_bytes, workspace_layout,
+    stem_score, stem_score_select, stem_tpd_budgets_host, stem_tpd_topk, workspace_bytes, workspace_layout,
+    bsa_prefill_inloop,
 )

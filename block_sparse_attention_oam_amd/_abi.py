@@ -26,7 +26,7 @@ MAX_REQS = 256
 
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
            "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
-           "bsa_prefill_inloop"]
+           "bsa_prefill_inloop", "stem_score_select"]
 
 
 class StemError(RuntimeError):
@@ -81,8 +81,9 @@ def lib() -> ctypes.CDLL:
         L.stem_tpd_topk.argtypes = [P, vp, i64, i32, i32, i32, i32, vp, i32, vp, vp]
         L.bsa_prefill.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
+        L.stem_score_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
         for name in ("stem_block_counts", "stem_workspace_layout", "stem_tpd_budgets_host", "stem_score",
-                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop"):
+                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -184,6 +185,17 @@ def stem_tpd_topk(p: Problem, scores, rho: tuple, mu: tuple, mask, counts, strea
     _check(lib().stem_tpd_topk(p.ref, _ptr(scores), int(scores.shape[-1]), int(rho[0]), int(rho[1]),
                                int(mu[0]), int(mu[1]), _ptr(mask), int(mask.shape[-1]), _ptr(counts),
                                _stream(stream)))
+
+
+def stem_score_select(p: Problem, q, k, v, beta: float, rho: tuple, mu: tuple, mask, counts, ws,
+                      stream=None) -> None:
+    """Pooling, scoring and selection in one call, without the score tensor (same mask and counts as
+    stem_score followed by stem_tpd_topk)."""
+    words = int(mask.shape[-1]) if mask is not None else 0
+    ws_bytes = int(ws.numel() * ws.element_size()) if ws is not None else 0
+    _check(lib().stem_score_select(p.ref, _ptr(q), _ptr(k), _ptr(v), float(beta), int(rho[0]), int(rho[1]),
+                                   int(mu[0]), int(mu[1]), _ptr(mask), words, _ptr(counts), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
 
 
 def bsa_prefill(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float = 0.0, stream=None) -> None:

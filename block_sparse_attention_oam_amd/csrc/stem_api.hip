@@ -214,15 +214,11 @@ int stem_tpd_budgets_host(int32_t n, int32_t rho_num, int32_t rho_den, int32_t m
   return ok();
 }
 
-int stem_score(const stem_problem* p, const void* q, const void* k, const void* v, float beta, float* scores,
-               int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream) {
-  Plan pl;
-  int st = make_plan(p, &pl);
-  if (st != STEM_OK) return st;
-  if (!q || !k || !v || !scores) return fail(STEM_E_INVALID_ARG, "q, k, v and scores must be non-NULL");
-  if (score_row_stride < pl.max_n)
-    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d blocks of the longest request",
-                (long long)score_row_stride, pl.max_n);
+// Validation shared by the entry points that pool (stem_score, stem_score_select) and the pooling launch.
+static int check_pool_args(const stem_problem* p, const Plan& pl, const void* q, const void* k, const void* v,
+                           float beta, void* ws, size_t ws_bytes) {
+  (void)p;
+  if (!q || !k || !v) return fail(STEM_E_INVALID_ARG, "q, k and v must be non-NULL");
   if (!isfinite(beta)) return fail(STEM_E_INVALID_ARG, "beta is not finite");
   size_t oq, okk, om, need;
   layout(pl, &oq, &okk, &om, &need);
@@ -231,10 +227,13 @@ int stem_score(const stem_problem* p, const void* q, const void* k, const void* 
   if (((uintptr_t)ws & 255) != 0) return fail(STEM_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15)
     return fail(STEM_E_INVALID_ARG, "q, k and v must be 16-byte aligned");
-  st = check_device();
-  if (st != STEM_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
+  return STEM_OK;
+}
 
+static hipError_t launch_pooling(const stem_problem* p, const Plan& pl, const void* q, const void* k, const void* v,
+                                 void* ws, hipStream_t s) {
+  size_t oq, okk, om, need;
+  layout(pl, &oq, &okk, &om, &need);
   PoolArgs pa;
   pa.q = q;
   pa.k = k;
@@ -256,13 +255,32 @@ int stem_score(const stem_problem* p, const void* q, const void* k, const void* 
   pa.kv_chunks = (p->hkv * p->head_dim / epl + 255) / 256;
   pa.kv = pl.kv;
   pa.rt = pl.rt;
-  hipError_t e = launch_pool(pa, p->dtype, s);
+  return launch_pool(pa, p->dtype, s);
+}
+
+int stem_score(const stem_problem* p, const void* q, const void* k, const void* v, float beta, float* scores,
+               int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  if (!scores) return fail(STEM_E_INVALID_ARG, "q, k, v and scores must be non-NULL");
+  if (score_row_stride < pl.max_n)
+    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d blocks of the longest request",
+                (long long)score_row_stride, pl.max_n);
+  st = check_pool_args(p, pl, q, k, v, beta, ws, ws_bytes);
+  if (st != STEM_OK) return st;
+  st = check_device();
+  if (st != STEM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_pooling(p, pl, q, k, v, ws, s);
   if (e != hipSuccess) return hip_status(e, "pool launch");
 
+  size_t oq, okk, om, need;
+  layout(pl, &oq, &okk, &om, &need);
   ScoreArgs sa;
-  sa.qbar = pa.qbar;
-  sa.kbar = pa.kbar;
-  sa.M = pa.M;
+  sa.qbar = (const float*)((char*)ws + oq);
+  sa.kbar = (const float*)((char*)ws + okk);
+  sa.M = (const float*)((char*)ws + om);
   sa.scores = scores;
   sa.stride = score_row_stride;
   sa.NB = pl.NB;
@@ -274,6 +292,59 @@ int stem_score(const stem_problem* p, const void* q, const void* k, const void* 
   sa.rt = pl.rt;
   e = launch_score(sa, pl.max_n, p->num_reqs, s);
   return hip_status(e, "score launch");
+}
+
+// Budget and mask arguments shared by stem_tpd_topk and stem_score_select.
+static int check_select_args(const Plan& pl, int32_t rho_num, int32_t rho_den, int32_t mu_num, int32_t mu_den,
+                             const uint32_t* mask, int32_t mask_row_words, const int32_t* counts) {
+  if (!mask || !counts) return fail(STEM_E_INVALID_ARG, "mask and counts must be non-NULL");
+  if (mask_row_words < (pl.max_n + 31) / 32)
+    return fail(STEM_E_INVALID_ARG, "mask_row_words = %d < %d", mask_row_words, (pl.max_n + 31) / 32);
+  int st = check_rational("rho", rho_num, rho_den, true);
+  if (st != STEM_OK) return st;
+  st = check_rational("mu", mu_num, mu_den, false);
+  if (st != STEM_OK) return st;
+  return check_budget_range(pl.max_n, rho_den, mu_num, mu_den);
+}
+
+int stem_score_select(const stem_problem* p, const void* q, const void* k, const void* v, float beta,
+                      int32_t rho_num, int32_t rho_den, int32_t mu_num, int32_t mu_den, uint32_t* mask,
+                      int32_t mask_row_words, int32_t* counts, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  st = check_pool_args(p, pl, q, k, v, beta, ws, ws_bytes);
+  if (st != STEM_OK) return st;
+  st = check_select_args(pl, rho_num, rho_den, mu_num, mu_den, mask, mask_row_words, counts);
+  if (st != STEM_OK) return st;
+  if (pl.max_n > 2048)
+    return fail(STEM_E_UNSUPPORTED, "fused scoring and selection supports up to 2048 blocks per request");
+  st = check_device();
+  if (st != STEM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_pooling(p, pl, q, k, v, ws, s);
+  if (e != hipSuccess) return hip_status(e, "pool launch");
+  size_t oq, okk, om, need;
+  layout(pl, &oq, &okk, &om, &need);
+  ScoreTopkArgs a;
+  a.qbar = (const float*)((char*)ws + oq);
+  a.kbar = (const float*)((char*)ws + okk);
+  a.M = (const float*)((char*)ws + om);
+  a.mask = mask;
+  a.mask_words = mask_row_words;
+  a.counts = counts;
+  a.NB = pl.NB;
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.d = p->head_dim;
+  a.beta = beta;
+  a.inv_sqrt_d = 1.0f / sqrtf((float)p->head_dim);
+  a.rho_num = rho_num;
+  a.rho_den = rho_den;
+  a.mu_num = mu_num;
+  a.mu_den = mu_den;
+  a.rt = pl.rt;
+  return hip_status(launch_score_topk(a, pl.max_n, p->num_reqs, s), "score-select launch");
 }
 
 int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_stride, int32_t rho_num,
@@ -288,11 +359,7 @@ int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_
   if (mask_row_words < (pl.max_n + 31) / 32)
     return fail(STEM_E_INVALID_ARG, "mask_row_words = %d < %d", mask_row_words, (pl.max_n + 31) / 32);
   if (pl.max_n > 4096) return fail(STEM_E_UNSUPPORTED, "selection supports up to 4096 blocks per request");
-  st = check_rational("rho", rho_num, rho_den, true);
-  if (st != STEM_OK) return st;
-  st = check_rational("mu", mu_num, mu_den, false);
-  if (st != STEM_OK) return st;
-  st = check_budget_range(pl.max_n, rho_den, mu_num, mu_den);
+  st = check_select_args(pl, rho_num, rho_den, mu_num, mu_den, mask, mask_row_words, counts);
   if (st != STEM_OK) return st;
   st = check_device();
   if (st != STEM_OK) return st;

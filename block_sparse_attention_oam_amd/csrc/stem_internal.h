@@ -60,6 +60,20 @@ struct TopkArgs {
   ReqTable rt;
 };
 
+struct ScoreTopkArgs {
+  const float* qbar;
+  const float* kbar;
+  const float* M;
+  uint32_t* mask;
+  int32_t mask_words;
+  int32_t* counts;
+  int64_t NB;
+  int32_t hq, hkv, d;
+  float beta, inv_sqrt_d;
+  int32_t rho_num, rho_den, mu_num, mu_den;
+  ReqTable rt;
+};
+
 struct BsaArgs {
   const void* q;
   const void* k;
@@ -84,6 +98,7 @@ struct BsaArgs {
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_n, int num_reqs, hipStream_t s);
+hipError_t launch_score_topk(const ScoreTopkArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int head_dim, bool paged, bool masked, hipStream_t s);
 bool bsa_bf16_supported(int dtype, int head_dim, int block);
 hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s);

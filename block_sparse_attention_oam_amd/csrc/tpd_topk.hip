@@ -15,7 +15,7 @@
 //   4. keys above the threshold are selected, then equal keys in increasing j until k are taken (ties go
 //      to the lower block index); each ballot is directly two 32-bit words of the packed mask row.
 // Bound: reading the causal half of the score rows (HBM) plus ~32 ballot rounds per row (ALU).
-#include "stem_internal.h"
+#include "select_common.h"
 
 namespace stem {
 
@@ -23,41 +23,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 8;
-
-// Order-preserving map float -> uint32 (larger float, larger key); -0 is folded onto +0.
-__device__ __forceinline__ uint32_t ord_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Number of leading indices in [0, n) where pred holds (pred true on a prefix), via 64-ary search.
-// Indices are 32-bit (see the note on 64-bit compares in tpd_budget.h).
-template <typename Pred>
-__device__ __forceinline__ int32_t wave_prefix_count(int32_t n, int lane, Pred pred) {
-  int32_t lo = 0, hi = n;
-  while (lo < hi) {
-    const int32_t step = (hi - lo + 63) >> 6;
-    const int32_t x = lo + lane * step;
-    const bool t = (x < hi) && pred(x);
-    const int c = __popcll(__ballot(t));
-    if (c == 0) {
-      hi = lo;
-    } else {
-      lo = lo + (c - 1) * step + 1;
-      hi = min(hi, lo - 1 + step);
-    }
-  }
-  return lo;
-}
-
-__device__ TpdPlan wave_plan(int32_t n, const TopkArgs& a, int lane) {
-  TpdPlan s = tpd_plan_init(n, a.rho_num, a.rho_den, a.mu_num, a.mu_den);
-  const int32_t p = wave_prefix_count(n, lane, [&](int32_t i) { return tpd_capped(s, i); });
-  const int32_t q = wave_prefix_count(n, lane, [&](int32_t m) { return !tpd_floored(s, m); });
-  tpd_plan_finish(s, p, q);
-  return s;
-}
 
 template <int NS>
 __global__ __launch_bounds__(kWaves * 64) void topk_kernel(TopkArgs a) {
@@ -69,8 +34,7 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(TopkArgs a) {
   const int lane = threadIdx.x % 64;
   const int i_begin = (blockIdx.x * kWaves + wave) * kRowsPerWave;
   if (i_begin >= n) return;
-  const TpdPlan plan = wave_plan(n, a, lane);
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const TpdPlan plan = wave_plan(n, a.rho_num, a.rho_den, a.mu_num, a.mu_den, lane);
   const int i_end = min(i_begin + kRowsPerWave, n);
 
   for (int i = i_begin; i < i_end; ++i) {
@@ -84,36 +48,7 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(TopkArgs a) {
       const int j = lane + 64 * s;
       key[s] = (s < nslot && j <= i) ? ord_key(srow[j]) : 0u;
     }
-    // k-th largest key: the largest tau with #{key >= tau} >= k (valid keys are >= 0x007FFFFF > 0)
-    uint32_t tau = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tau | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        if (s < nslot) cnt += __popcll(__ballot(key[s] >= cand));
-      if (cnt >= k) tau = cand;
-    }
-    int gt = 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      if (s < nslot) gt += __popcll(__ballot(key[s] > tau));
-    const int need = k - gt;
-    int taken = 0;
-    uint32_t* mrow = a.mask + row * a.mask_words;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (s < nslot) {
-        const uint64_t eq = __ballot(key[s] == tau);
-        const int rank = taken + __popcll(eq & below);
-        const bool sel = key[s] > tau || (key[s] == tau && rank < need);
-        const uint64_t selm = __ballot(sel);
-        taken += __popcll(eq);
-        if (lane < 2 && 2 * s + lane < a.mask_words)
-          mrow[2 * s + lane] = lane == 0 ? (uint32_t)selm : (uint32_t)(selm >> 32);
-      }
-    }
-    for (int w = 2 * nslot + lane; w < a.mask_words; w += 64) mrow[w] = 0u;
+    select_row<NS>(key, nslot, k, lane, a.mask + row * a.mask_words, a.mask_words);
     if (lane == 0) a.counts[row] = k;
   }
 }

@@ -53,6 +53,10 @@ class StemPrefill:
     def select(self, rho=(25, 100), mu=(7, 10), stream=None):
         _abi.stem_tpd_topk(self.p, self.scores, rho, mu, self.mask, self.counts, stream)
 
+    def score_select(self, q, k, v, beta=0.2, rho=(25, 100), mu=(7, 10), stream=None):
+        """Pooling, scoring and selection fused (no score tensor); fills mask and counts."""
+        _abi.stem_score_select(self.p, q, k, v, beta, rho, mu, self.mask, self.counts, self.ws, stream)
+
     def attend(self, q, k, v, mask="selected", lse=True, softmax_scale=0.0, stream=None, inloop=False):
         """inloop=True runs the comparison variant that tests the mask inside the loop."""
         m = self.mask if isinstance(mask, str) and mask == "selected" else mask

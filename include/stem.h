@@ -124,6 +124,18 @@ int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_
                   int32_t rho_den, int32_t mu_num, int32_t mu_den, uint32_t* mask, int32_t mask_row_words,
                   int32_t* counts, void* stream);
 
+/* Stages 1 + 2 fused: the score tensor never reaches memory ---------------------------------------- */
+/* Pools Q/K/V into the workspace exactly as stem_score does, then computes each row's block scores on
+ * chip and selects from them exactly as stem_tpd_topk does: mask and counts are bit-identical to
+ * stem_score followed by stem_tpd_topk with the same arguments, without the score tensor (NB x max n
+ * floats per query head) being written or read.  Arguments as in those two calls; requests of up to 2048
+ * blocks (STEM_E_UNSUPPORTED beyond).
+ * Source: "HPC-Stem：评估选块，快几十倍" (scoring, budget and selection fused so that no intermediate tensor
+ * goes through HBM). */
+int stem_score_select(const stem_problem* p, const void* q, const void* k, const void* v, float beta,
+                      int32_t rho_num, int32_t rho_den, int32_t mu_num, int32_t mu_den, uint32_t* mask,
+                      int32_t mask_row_words, int32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
 /* Stage 3: block-sparse attention ----------------------------------------------------------------- */
 /* For query token t of query block i, head h: out = softmax over visible keys s of (q_t . k_s) * scale,
  * applied to v_s, where s is visible when its block j is selected in mask row (h, i) (j <= i) and s <= t

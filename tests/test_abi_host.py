@@ -141,6 +141,8 @@ def test_invalid_problem_is_rejected_by_every_entry_point(kw, msg):
         lambda: stem.stem_tpd_topk(p, T(shape=(1, 1, 64)), (1, 4), (7, 10), T(shape=(1, 1, 2)), T(), stream=0),
         lambda: stem.bsa_prefill(p, T(), T(), T(), None, T(), stream=0),
         lambda: _abi.bsa_prefill_inloop(p, T(), T(), T(), T(shape=(8, 24, 1)), T(), stream=0),
+        lambda: stem.stem_score_select(p, T(), T(), T(), 0.2, (1, 4), (7, 10), T(shape=(1, 1, 2)), T(),
+                                       T(shape=(1 << 30,), elem=1), stream=0),
     ]
     for c in calls:
         with pytest.raises(stem.StemError) as e:
@@ -213,6 +215,40 @@ def test_inloop_variant_argument_errors():
         with pytest.raises(stem.StemError) as e:
             A.bsa_prefill_inloop(q, T(), T(), T(), T(shape=(8, nb, (mx + 31) // 32)), T(), stream=0)
         assert e.value.status == A.STEM_E_UNSUPPORTED, (kw, str(e.value))
+
+
+def test_score_select_argument_errors():
+    """The fused scoring + selection entry point validates the union of stem_score's and stem_tpd_topk's
+    arguments (no score tensor) and supports requests of up to 2048 blocks."""
+    T = _FakeTensor
+    p = _prob()  # NB = 24, max_n = 16
+    need = stem.workspace_bytes(p)
+    ws = T(shape=(need,), elem=1)
+    ok = dict(q=T(), k=T(), v=T(), beta=0.2, rho=(1, 4), mu=(7, 10), mask=T(shape=(8, 24, 1)), counts=T(), ws=ws)
+    cases = [
+        (dict(q=None), "non-NULL"),
+        (dict(mask=None), "non-NULL"),
+        (dict(counts=None), "non-NULL"),
+        (dict(ws=T(shape=(need - 1,), elem=1)), "workspace"),
+        (dict(beta=float("nan")), "beta"),
+        (dict(mask=T(shape=(8, 24, 0))), "mask_row_words"),
+        (dict(rho=(5, 4)), "rho"),
+        (dict(mu=(0, 10)), "mu"),
+        (dict(v=T(addr=0x10008)), "aligned"),
+    ]
+    for kw, msg in cases:
+        a = dict(ok)
+        a.update(kw)
+        with pytest.raises(stem.StemError) as e:
+            stem.stem_score_select(p, a["q"], a["k"], a["v"], a["beta"], a["rho"], a["mu"], a["mask"], a["counts"],
+                                   a["ws"], stream=0)
+        assert msg in str(e.value), (kw, str(e.value))
+    big = _prob(cu_seqlens=[0, 2049 * 128])
+    nb, mx = stem.block_counts(big)
+    with pytest.raises(stem.StemError) as e:
+        stem.stem_score_select(big, T(), T(), T(), 0.2, (1, 4), (7, 10), T(shape=(8, nb, (mx + 31) // 32)), T(),
+                               T(shape=(stem.workspace_bytes(big),), elem=1), stream=0)
+    assert e.value.status == _abi.STEM_E_UNSUPPORTED
 
 
 def test_last_error_is_cleared_by_a_successful_call():

@@ -227,6 +227,64 @@ def test_full_size_workload(dev, name):
     assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
 
 
+# ------------------------------------------------------------------------------------ fused scoring + selection
+def _fused_vs_two_stage(p, x, dev):
+    """Masks and counts from stem_score + stem_tpd_topk and from stem_score_select on the same inputs."""
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    kw = {}
+    if p.dtype == "fp8":
+        kw = dict(q_scale=upload(x["q_scale"]), k_scale=upload(x["k_scale"]), v_scale=upload(x["v_scale"]))
+    if p.paged:
+        prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype, page_table=upload(x["page_table"]),
+                                 page_size=p.page_size, num_pages=x["k_pages"].shape[0], **kw)
+        k, v = upload(x["k_pages"]), upload(x["v_pages"])
+    else:
+        prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype, **kw)
+        k, v = upload(x["k"]), upload(x["v"])
+    q = upload(x["q"])
+    L = StemPrefill(prob, dev)
+    rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
+    L.score(q, k, v, p.beta)
+    L.select(rho, mu)
+    m1, c1 = L.mask.clone(), L.counts.clone()
+    L.mask.fill_(-1)
+    L.counts.fill_(-1)
+    L.ws.zero_()
+    L.score_select(q, k, v, p.beta, rho, mu)
+    torch.cuda.synchronize()
+    return L, m1, c1
+
+
+@pytest.mark.parametrize("name,over", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
+def test_fused_score_select_equals_two_stage(dev, name, over):
+    p = synth.make_problem(name, **over)
+    x = synth.make_inputs(p, seed=0)
+    L, m1, c1 = _fused_vs_two_stage(p, x, dev)
+    assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
+
+
+def test_fused_score_select_matches_oracle(dev):
+    p = synth.make_problem("llama_32k_bf16", lens=(1500, 700), hq=8, hkv=2)
+    x = synth.make_inputs(p, seed=9)
+    ref1 = sc.oracle_stage1(p, x)
+    S_list = [s for *_, s in ref1]
+    budgets = sc.oracle_budgets(p)
+    L, _, _ = _fused_vs_two_stage(p, x, dev)
+    sc.check_selection(p, S_list, budgets, L.mask.cpu().numpy().view(np.uint32), L.counts.cpu().numpy())
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["llama_32k_bf16", "llama_128k_bf16", "w8a8_128k_fp8", "paged_ragged_bf16"])
+def test_fused_score_select_full_size(dev, name):
+    p = synth.make_problem(name)
+    _log(f"[fused] {name}")
+    x = synth.make_inputs(p, seed=0)
+    L, m1, c1 = _fused_vs_two_stage(p, x, dev)
+    assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
+
+
 # ------------------------------------------------------------------------------------ in-loop skip variant
 def _inloop_vs_list(p, x, dev, mask_dev=None):
     """Run bsa_prefill and bsa_prefill_inloop on the same mask (the GPU's own selection by default);
