@@ -21,6 +21,10 @@ Readings of points the pages leave open (each one is listed, with its reason, in
   R8  ties in selection go to the lower block index.
   R9  softmax scale 1/sqrt(d); causal rule key position <= query position inside a request.
   R12 a query row with no visible key has output 0 and LSE = -inf.
+  R15 the naive comparison form of the metric samples `samples` queries per block at offsets
+      s * (B / samples) (clamped to the request's last token), takes each one's softmax over its visible
+      keys, sums the probability mass per key block, averages over the block's samples, and scores
+      ln(mean mass) + beta * M[g][j].
 
 Parity pins (tests under `tests/`, marked "not gpu"): every function below is pinned by something other
 than itself -- brute-force token-level scores, an independent floating-point bisection of the TPD solve,
@@ -40,6 +44,7 @@ __all__ = [
     "pool_blocks", "value_log_magnitude", "oam_block_scores", "oam_token_scores",
     "tpd_total", "tpd_solve", "tpd_budgets", "select_row", "select_all",
     "attention_rows", "block_sparse_attention", "dense_causal_attention", "causal_pairs",
+    "sampled_query_positions", "naive_block_scores",
 ]
 
 
@@ -344,3 +349,50 @@ def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: f
         O[:, h] = (p @ v[:, g]) / l[:, None]
         lse[h] = m + np.log(l)
     return O, lse
+
+
+# ----------------------------------------------------------------------------------------------------
+# Comparison path: the naive, token-level form of the metric  ([Arch] "HPC-Stem：评估选块，快几十倍", which
+# contrasts the one-GEMM scoring with computing attention probabilities token by token and gathering them
+# into blocks)
+# ----------------------------------------------------------------------------------------------------
+def sampled_query_positions(L: int, B: int, samples: int) -> np.ndarray:
+    """Reading R15: [n][samples] token positions, block i's sample s at i*B + s*(B/samples), clamped to
+    L - 1 (a partial last block repeats its last token)."""
+    n = -(-L // B)
+    step = B // samples
+    return np.array([[min(i * B + s * step, L - 1) for s in range(samples)] for i in range(n)], dtype=np.int64)
+
+
+def naive_block_scores(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, beta: float, samples: int,
+                       scale: float | None = None) -> np.ndarray:
+    """Naive block scores of one request (reading R15).
+
+    For block i and head h, each sampled query t takes the softmax of q_t . k_tau * scale over the keys
+    tau <= t (KV head g = h // (Hq/Hkv)); the probability mass falling in key block j is summed, averaged
+    over the block's samples, and S[h][i][j] = ln(mean mass) + beta * M[g][j] for j <= i (NaN above the
+    diagonal).  q [L][Hq][d], k/v [L][Hkv][d] float64.
+    """
+    L, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    n = -(-L // B)
+    M = value_log_magnitude(v, B)
+    pos = sampled_query_positions(L, B, samples)
+    S = np.full((hq, n, n), np.nan)
+    for h in range(hq):
+        g = h // grp
+        for i in range(n):
+            mass = np.zeros(n)
+            for t in pos[i]:
+                logits = (k[: t + 1, g] @ q[t, h]) * scale
+                p = np.exp(logits - logits.max())
+                p /= p.sum()
+                for j in range(i + 1):
+                    mass[j] += p[j * B: min((j + 1) * B, t + 1)].sum()
+            mass /= samples
+            with np.errstate(divide="ignore"):
+                S[h, i, : i + 1] = np.log(mass[: i + 1]) + beta * M[g, : i + 1]
+    return S

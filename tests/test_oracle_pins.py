@@ -304,3 +304,63 @@ def test_rows_subset_matches_full_run():
     Os, lses = oracle.block_sparse_attention(q, k, v, mask, B, rows=[(3, 4), (0, 2)])
     assert np.array_equal(Os[32:40, 3], O[32:40, 3]) and np.array_equal(lses[0, 16:24], lse[0, 16:24])
     assert np.isnan(Os[0, 1, 0])
+
+
+# ------------------------------------------------------------------------------------ naive comparator
+def test_naive_sampled_positions():
+    pos = oracle.sampled_query_positions(300, 64, 4)
+    assert pos.tolist()[0] == [0, 16, 32, 48]
+    assert pos.tolist()[-1] == [256, 272, 288, 299]  # the partial last block repeats its last token
+
+
+def test_naive_scores_uniform_keys_closed_form():
+    """All keys equal: every softmax is uniform over the t + 1 visible keys, so the mass of block j is
+    |block j within [0, t]| / (t + 1) (beta = 0 isolates the routing term)."""
+    rng = np.random.default_rng(1)
+    L, B, S = 200, 32, 4
+    q = rng.normal(size=(L, 2, 8))
+    k = np.tile(rng.normal(size=(1, 1, 8)), (L, 1, 1))
+    v = rng.normal(size=(L, 1, 8))
+    got = oracle.naive_block_scores(q, k, v, B, 0.0, S)
+    pos = oracle.sampled_query_positions(L, B, S)
+    n = -(-L // B)
+    for i in range(n):
+        for j in range(i + 1):
+            want = np.mean([max(0, min((j + 1) * B, t + 1) - j * B) / (t + 1) for t in pos[i]])
+            assert abs(got[0, i, j] - math.log(want)) < 1e-12
+            assert abs(got[1, i, j] - math.log(want)) < 1e-12
+
+
+def test_naive_scores_mass_sums_to_one():
+    """Probability conservation: for each row the block masses (exp of score minus beta M) add up to 1."""
+    rng = np.random.default_rng(2)
+    L, B = 333, 32
+    q, k, v = rng.normal(size=(L, 4, 16)), rng.normal(size=(L, 2, 16)), rng.normal(size=(L, 2, 16))
+    S = oracle.naive_block_scores(q, k, v, B, 0.3, 8)
+    M = oracle.value_log_magnitude(v, B)
+    for h in range(4):
+        for i in range(S.shape[1]):
+            assert abs(np.exp(S[h, i, : i + 1] - 0.3 * M[h // 2, : i + 1]).sum() - 1.0) < 1e-12
+
+
+def test_naive_scores_against_masked_softmax_over_the_full_matrix():
+    """Brute force by another route: the full token-level logit matrix, an additive causal mask, torch's
+    softmax, then block sums of the sampled rows."""
+    rng = np.random.default_rng(3)
+    L, B, S, hq, hkv, d = 150, 16, 2, 4, 2, 8
+    q, k, v = rng.normal(size=(L, hq, d)), rng.normal(size=(L, hkv, d)), rng.normal(size=(L, hkv, d))
+    got = oracle.naive_block_scores(q, k, v, B, 0.5, S)
+    M = oracle.value_log_magnitude(v, B)
+    pos = oracle.sampled_query_positions(L, B, S)
+    n = -(-L // B)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        logits = torch.tensor(q[:, h] @ k[:, g].T / math.sqrt(d))
+        logits = logits.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+        P = torch.softmax(logits, dim=1).numpy()
+        pad = np.zeros((L, n * B))
+        pad[:, :L] = P
+        mass = pad.reshape(L, n, B).sum(axis=2)  # [t][j]
+        for i in range(n):
+            want = np.log(mass[pos[i]].mean(axis=0)[: i + 1]) + 0.5 * M[g, : i + 1]
+            assert np.max(np.abs(got[h, i, : i + 1] - want)) < 1e-12
