@@ -197,6 +197,41 @@ def measure_ablations(L, q, k, v, p, torch, reps=3):
     return res
 
 
+def measure_naive(L, q, k, v, p, dev, torch, score_ms, fused_ms, samples=4):
+    """The naive token-level scoring (sampled queries, softmax, block mass; every step through HBM) on the
+    same inputs: its time, its intermediate bytes, and how its selection compares with the pooled one."""
+    from block_sparse_attention_oam_amd import _abi
+
+    rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
+    ref = L.mask.cpu().numpy().view(np.uint32).copy()
+    nbytes = _abi.naive_workspace_bytes(L.p, samples)
+    try:
+        nws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    except RuntimeError as e:  # pragma: no cover - memory
+        return {"skipped": f"could not allocate {nbytes} bytes: {e}"}
+    _abi.stem_naive_score(L.p, q, k, v, p.beta, samples, L.scores, L.ws, nws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(2):
+        _abi.stem_naive_score(L.p, q, k, v, p.beta, samples, L.scores, L.ws, nws)
+    b.record()
+    torch.cuda.synchronize()
+    naive_ms = a.elapsed_time(b) / 2
+    L.select(rho, mu)
+    torch.cuda.synchronize()
+    stats = selection_stats(p, L.mask.cpu().numpy().view(np.uint32), ref)
+    del nws
+    torch.cuda.empty_cache()
+    L.score(q, k, v, p.beta)
+    L.select(rho, mu)
+    torch.cuda.synchronize()
+    return {"samples_per_block": samples, "ms": round(naive_ms, 3), "intermediate_bytes": int(nbytes),
+            "pooled_score_ms": round(score_ms, 4), "speedup_of_pooled_scoring": round(naive_ms / score_ms, 1),
+            "speedup_of_fused_score_select": round(naive_ms / fused_ms, 1),
+            "jaccard_with_pooled_selection": stats["jaccard_vs_default"]}
+
+
 def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
     """The oracle, as it stands, on a bounded sample of rows of the same workload: for each sampled
     (query head, query block) row it pools, scores, takes the TPD budget, selects and attends.
@@ -347,6 +382,9 @@ def main():
             "same_mask": bool(torch.equal(ref_mask, L.mask)),
             "score_tensor_bytes_avoided": int(4 * sum(p.hq * p.nblocks(r) * (p.nblocks(r) + 1) for r in range(len(p.lens)))),
         }
+        if p.dtype == "bf16" and not p.paged:
+            log("[bench] naive token-level scoring (comparison path)")
+            out["naive_scoring"] = measure_naive(L, q, k, v, p, dev, torch, float(stage_ms[0]), fused_ms)
         log("[bench] dense-causal run of the same kernel")
         dense_ms = time_bsa(L, q, k, v, None, 3, torch)
         dflops = 4 * p.d * dense_pairs(p)

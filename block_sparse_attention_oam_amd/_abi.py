@@ -26,7 +26,7 @@ MAX_REQS = 256
 
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
            "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
-           "bsa_prefill_inloop", "stem_score_select"]
+           "bsa_prefill_inloop", "stem_score_select", "stem_naive_workspace_bytes", "stem_naive_score"]
 
 
 class StemError(RuntimeError):
@@ -82,8 +82,11 @@ def lib() -> ctypes.CDLL:
         L.bsa_prefill.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.stem_score_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
+        L.stem_naive_workspace_bytes.argtypes = [P, i32]
+        L.stem_naive_workspace_bytes.restype = sz
+        L.stem_naive_score.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, vp, i64, vp, sz, vp, sz, vp]
         for name in ("stem_block_counts", "stem_workspace_layout", "stem_tpd_budgets_host", "stem_score",
-                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select"):
+                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select", "stem_naive_score"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,6 +199,21 @@ def stem_score_select(p: Problem, q, k, v, beta: float, rho: tuple, mu: tuple, m
     _check(lib().stem_score_select(p.ref, _ptr(q), _ptr(k), _ptr(v), float(beta), int(rho[0]), int(rho[1]),
                                    int(mu[0]), int(mu[1]), _ptr(mask), words, _ptr(counts), _ptr(ws), ws_bytes,
                                    _stream(stream)))
+
+
+def naive_workspace_bytes(p: Problem, samples: int) -> int:
+    n = lib().stem_naive_workspace_bytes(p.ref, int(samples))
+    if n == 0:
+        raise StemError(STEM_E_INVALID_ARG, lib().stem_last_error().decode())
+    return int(n)
+
+
+def stem_naive_score(p: Problem, q, k, v, beta: float, samples: int, scores, ws, naive_ws, stream=None) -> None:
+    """The naive token-level block scores (comparison path), in stem_score's layout."""
+    _check(lib().stem_naive_score(p.ref, _ptr(q), _ptr(k), _ptr(v), float(beta), int(samples), _ptr(scores),
+                                  int(scores.shape[-1]), _ptr(ws), int(ws.numel() * ws.element_size()),
+                                  _ptr(naive_ws), int(naive_ws.numel() * naive_ws.element_size())
+                                  if naive_ws is not None else 0, _stream(stream)))
 
 
 def bsa_prefill(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float = 0.0, stream=None) -> None:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libstem.so")
 
-SOURCES = ["stem_api.hip", "pool_score.hip", "tpd_topk.hip", "score_topk.hip", "bsa_fwd.hip", "bsa_bf16.hip", "bsa_fp8.hip"]
+SOURCES = ["stem_api.hip", "pool_score.hip", "tpd_topk.hip", "score_topk.hip", "naive_score.hip", "bsa_fwd.hip", "bsa_bf16.hip", "bsa_fp8.hip"]
 
 # Packed-fp32 VALU ops are disabled for all device code; the host pass warns that it does not know the
 # feature, which is harmless.

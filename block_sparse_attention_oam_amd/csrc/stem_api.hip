@@ -379,6 +379,92 @@ int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_
   return hip_status(launch_topk(ta, pl.max_n, p->num_reqs, (hipStream_t)stream), "topk launch");
 }
 
+// ---- the naive comparison path
+static void naive_layout(const Plan& pl, int32_t samples, int64_t* row_stride, int64_t* mass_stride,
+                         int64_t* rows_max, size_t* off_mass, size_t* total) {
+  const stem_problem* p = pl.p;
+  *row_stride = ((int64_t)pl.max_len + 63) / 64 * 64;
+  *mass_stride = ((int64_t)pl.max_n + 63) / 64 * 64;
+  *rows_max = (int64_t)pl.max_n * samples;
+  const size_t buf = (size_t)p->hq * (size_t)(*rows_max) * (size_t)(*row_stride) * sizeof(float);
+  const size_t mass = (size_t)p->hq * (size_t)(*rows_max) * (size_t)(*mass_stride) * sizeof(float);
+  *off_mass = align256(buf);
+  *total = *off_mass + align256(mass);
+}
+
+static int check_naive(const stem_problem* p, const Plan& pl, int32_t samples) {
+  if (p->dtype != STEM_BF16 || p->kv_paged)
+    return fail(STEM_E_UNSUPPORTED, "the naive comparison path supports bf16 inputs with contiguous K/V");
+  if (samples < 1 || samples > p->block || p->block % samples != 0)
+    return fail(STEM_E_INVALID_ARG, "samples = %d must divide block = %d", samples, p->block);
+  (void)pl;
+  return STEM_OK;
+}
+
+size_t stem_naive_workspace_bytes(const stem_problem* p, int32_t samples) {
+  Plan pl;
+  if (make_plan(p, &pl) != STEM_OK || check_naive(p, pl, samples) != STEM_OK) return 0;
+  int64_t rs, ms, rm;
+  size_t om, total;
+  naive_layout(pl, samples, &rs, &ms, &rm, &om, &total);
+  return total;
+}
+
+int stem_naive_score(const stem_problem* p, const void* q, const void* k, const void* v, float beta,
+                     int32_t samples, float* scores, int64_t score_row_stride, void* ws, size_t ws_bytes,
+                     void* naive_ws, size_t naive_ws_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  st = check_naive(p, pl, samples);
+  if (st != STEM_OK) return st;
+  if (!scores) return fail(STEM_E_INVALID_ARG, "scores must be non-NULL");
+  if (score_row_stride < pl.max_n)
+    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d", (long long)score_row_stride, pl.max_n);
+  st = check_pool_args(p, pl, q, k, v, beta, ws, ws_bytes);
+  if (st != STEM_OK) return st;
+  int64_t rs, ms, rm;
+  size_t om_naive, need;
+  naive_layout(pl, samples, &rs, &ms, &rm, &om_naive, &need);
+  if (!naive_ws || naive_ws_bytes < need)
+    return fail(STEM_E_WORKSPACE, "naive workspace of %zu bytes given, %zu needed",
+                naive_ws ? naive_ws_bytes : (size_t)0, need);
+  if (((uintptr_t)naive_ws & 255) != 0) return fail(STEM_E_WORKSPACE, "naive workspace must be 256-byte aligned");
+  st = check_device();
+  if (st != STEM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_pooling(p, pl, q, k, v, ws, s);  // M (and the pooled q, k, unused here)
+  if (e != hipSuccess) return hip_status(e, "pool launch");
+  size_t oq, okk, om, wneed;
+  layout(pl, &oq, &okk, &om, &wneed);
+  NaiveArgs a;
+  a.q = q;
+  a.k = k;
+  a.buf = (float*)naive_ws;
+  a.mass = (float*)((char*)naive_ws + om_naive);
+  a.M = (const float*)((char*)ws + om);
+  a.scores = scores;
+  a.row_stride = rs;
+  a.mass_stride = ms;
+  a.rows_max = rm;
+  a.stride = score_row_stride;
+  a.NB = pl.NB;
+  a.hq = p->hq;
+  a.hkv = p->hkv;
+  a.d = p->head_dim;
+  a.B = p->block;
+  a.samples = samples;
+  a.scale = 1.0f / sqrtf((float)p->head_dim);
+  a.beta = beta;
+  a.rt = pl.rt;
+  int32_t lens[STEM_MAX_REQS], nbl[STEM_MAX_REQS];
+  for (int r = 0; r < p->num_reqs; ++r) {
+    lens[r] = p->cu_seqlens[r + 1] - p->cu_seqlens[r];
+    nbl[r] = pl.rt.cu_blocks[r + 1] - pl.rt.cu_blocks[r];
+  }
+  return hip_status(launch_naive(a, lens, nbl, p->num_reqs, s), "naive launch");
+}
+
 static int prepare_bsa(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
                        int32_t mask_row_words, float softmax_scale, void* out, float* lse, Plan* pl, BsaArgs* ba) {
   int st = make_plan(p, pl);

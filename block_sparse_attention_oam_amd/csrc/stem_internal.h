@@ -74,6 +74,19 @@ struct ScoreTopkArgs {
   ReqTable rt;
 };
 
+struct NaiveArgs {
+  const void* q;
+  const void* k;
+  float* buf;     // [hq][rows_max][row_stride] logits, then probabilities
+  float* mass;    // [hq][rows_max][mass_stride] per-block probability mass
+  const float* M; // pooled ln||v|| means [hkv][NB]
+  float* scores;  // [hq][NB][stride]
+  int64_t row_stride, mass_stride, rows_max, stride, NB;
+  int32_t hq, hkv, d, B, samples;
+  float scale, beta;
+  ReqTable rt;
+};
+
 struct BsaArgs {
   const void* q;
   const void* k;
@@ -99,6 +112,8 @@ hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_score_topk(const ScoreTopkArgs& a, int max_n, int num_reqs, hipStream_t s);
+hipError_t launch_naive(const NaiveArgs& a, const int32_t* lens, const int32_t* nblocks, int num_reqs,
+                        hipStream_t s);
 hipError_t launch_bsa(const BsaArgs& a, int dtype, int head_dim, bool paged, bool masked, hipStream_t s);
 bool bsa_bf16_supported(int dtype, int head_dim, int block);
 hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s);

@@ -136,6 +136,22 @@ int stem_score_select(const stem_problem* p, const void* q, const void* k, const
                       int32_t rho_num, int32_t rho_den, int32_t mu_num, int32_t mu_den, uint32_t* mask,
                       int32_t mask_row_words, int32_t* counts, void* ws, size_t ws_bytes, void* stream);
 
+/* Comparison path: the naive, token-level form of the block score ----------------------------------- */
+/* For `samples` sampled queries per block (block i's sample s is token min(i*block + s*block/samples,
+ * L - 1)), the softmax of q_t . k_tau / sqrt(head_dim) over the keys tau <= t, the probability mass per key
+ * block j, averaged over block i's samples: S[h][i][j] = ln(mean mass) + beta * M[g][j] for j <= i, in
+ * stem_score's layout (stem_tpd_topk selects from it as usual).  Every step goes through memory: the
+ * token-level logits and probabilities (hq x max_n*samples x max L floats) live in naive_ws, DEVICE,
+ * naive_ws_bytes >= stem_naive_workspace_bytes(p, samples), 256-byte aligned; ws is stem_score's
+ * workspace (M is pooled there).  bf16 inputs with contiguous K/V only; samples must divide block.
+ * It exists to measure what the pooled one-GEMM scoring saves.
+ * Source: "HPC-Stem：评估选块，快几十倍" (the direct token-level computation needs intermediate tensors of
+ * tens of GB and is tens of times slower). */
+size_t stem_naive_workspace_bytes(const stem_problem* p, int32_t samples); /* 0 on invalid input */
+int stem_naive_score(const stem_problem* p, const void* q, const void* k, const void* v, float beta,
+                     int32_t samples, float* scores, int64_t score_row_stride, void* ws, size_t ws_bytes,
+                     void* naive_ws, size_t naive_ws_bytes, void* stream);
+
 /* Stage 3: block-sparse attention ----------------------------------------------------------------- */
 /* For query token t of query block i, head h: out = softmax over visible keys s of (q_t . k_s) * scale,
  * applied to v_s, where s is visible when its block j is selected in mask row (h, i) (j <= i) and s <= t

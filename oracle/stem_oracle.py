@@ -365,13 +365,14 @@ def sampled_query_positions(L: int, B: int, samples: int) -> np.ndarray:
 
 
 def naive_block_scores(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, beta: float, samples: int,
-                       scale: float | None = None) -> np.ndarray:
+                       scale: float | None = None, rows=None) -> np.ndarray:
     """Naive block scores of one request (reading R15).
 
     For block i and head h, each sampled query t takes the softmax of q_t . k_tau * scale over the keys
     tau <= t (KV head g = h // (Hq/Hkv)); the probability mass falling in key block j is summed, averaged
     over the block's samples, and S[h][i][j] = ln(mean mass) + beta * M[g][j] for j <= i (NaN above the
-    diagonal).  q [L][Hq][d], k/v [L][Hkv][d] float64.
+    diagonal).  q [L][Hq][d], k/v [L][Hkv][d] float64.  `rows` optionally restricts the work to (h, i)
+    pairs; the other rows stay NaN.
     """
     L, hq, d = q.shape
     hkv = k.shape[1]
@@ -382,17 +383,17 @@ def naive_block_scores(q: np.ndarray, k: np.ndarray, v: np.ndarray, B: int, beta
     M = value_log_magnitude(v, B)
     pos = sampled_query_positions(L, B, samples)
     S = np.full((hq, n, n), np.nan)
-    for h in range(hq):
+    todo = rows if rows is not None else [(h, i) for h in range(hq) for i in range(n)]
+    for h, i in todo:
         g = h // grp
-        for i in range(n):
-            mass = np.zeros(n)
-            for t in pos[i]:
-                logits = (k[: t + 1, g] @ q[t, h]) * scale
-                p = np.exp(logits - logits.max())
-                p /= p.sum()
-                for j in range(i + 1):
-                    mass[j] += p[j * B: min((j + 1) * B, t + 1)].sum()
-            mass /= samples
-            with np.errstate(divide="ignore"):
-                S[h, i, : i + 1] = np.log(mass[: i + 1]) + beta * M[g, : i + 1]
+        mass = np.zeros(n)
+        for t in pos[i]:
+            logits = (k[: t + 1, g] @ q[t, h]) * scale
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            for j in range(i + 1):
+                mass[j] += p[j * B: min((j + 1) * B, t + 1)].sum()
+        mass /= samples
+        with np.errstate(divide="ignore"):
+            S[h, i, : i + 1] = np.log(mass[: i + 1]) + beta * M[g, : i + 1]
     return S

@@ -285,6 +285,70 @@ def test_fused_score_select_full_size(dev, name):
     assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
 
 
+# ------------------------------------------------------------------------------------ naive comparison path
+def _naive_gpu(p, x, dev, samples):
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd import _abi
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype)
+    q, k, v = upload(x["q"]), upload(x["k"]), upload(x["v"])
+    L = StemPrefill(prob, dev)
+    nws = torch.empty(_abi.naive_workspace_bytes(prob, samples), dtype=torch.uint8, device=dev)
+    L.scores.fill_(float("nan"))
+    _abi.stem_naive_score(prob, q, k, v, p.beta, samples, L.scores, L.ws, nws)
+    L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
+    torch.cuda.synchronize()
+    del nws
+    return L
+
+
+@pytest.mark.parametrize("lens,hq,hkv,d,block,samples", [
+    ((1000,), 4, 2, 128, 128, 4), ((300, 1, 129, 700), 4, 4, 128, 128, 1),
+    ((777,), 8, 1, 64, 64, 8), ((2000,), 2, 1, 128, 128, 128), ((640, 513), 4, 2, 128, 64, 16)])
+def test_naive_scores_match_oracle(dev, lens, hq, hkv, d, block, samples):
+    """The naive token-level scores (sampled queries, softmax, block mass) against the oracle's, and the
+    TPD selection made from them."""
+    p = synth.make_problem("llama_32k_bf16", lens=lens, hq=hq, hkv=hkv, d=d, block=block)
+    x = synth.make_inputs(p, seed=21)
+    L = _naive_gpu(p, x, dev, samples)
+    gs = L.scores.cpu().numpy()
+    cb = p.cu_blocks
+    S_list = []
+    worst = 0.0
+    for r, (a, b) in enumerate(sc.request_slices(p)):
+        q = sc.decode_q(p, x, a, b)
+        k = sc.decode_kv(p, x, r, "k")
+        v = sc.decode_kv(p, x, r, "v")
+        S = oracle.naive_block_scores(q, k, v, p.block, p.beta, samples)
+        n = S.shape[1]
+        tri = np.tril(np.ones((n, n), dtype=bool))
+        worst = max(worst, float(np.max(np.abs(gs[:, cb[r]:cb[r + 1], :n][:, tri] - S[:, tri]))))
+        S_list.append(S)
+    _log(f"[naive] {lens} samples {samples}: max abs score error {worst:.2e}")
+    assert worst < 2e-4
+    sc.check_selection(p, S_list, sc.oracle_budgets(p), L.mask.cpu().numpy().view(np.uint32),
+                       L.counts.cpu().numpy())
+
+
+@pytest.mark.timeout(600)
+def test_naive_scores_full_size_32k_sampled_rows(dev):
+    """At the 32K workload (4 samples per block) on sampled rows: each checked row's scores against the
+    oracle's."""
+    p = synth.make_problem("llama_32k_bf16")
+    x = synth.make_inputs(p, seed=0)
+    L = _naive_gpu(p, x, dev, 4)
+    gs = L.scores.cpu().numpy()
+    q = sc.decode_q(p, x, 0, p.lens[0])
+    k = sc.decode_kv(p, x, 0, "k")
+    v = sc.decode_kv(p, x, 0, "v")
+    rows = [(0, 0), (3, 17), (9, 128), (17, 200), (31, 255), (30, 254)]
+    S = oracle.naive_block_scores(q, k, v, p.block, p.beta, 4, rows=rows)
+    for h, i in rows:
+        err = np.max(np.abs(gs[h, i, : i + 1] - S[h, i, : i + 1]))
+        assert err < 2e-4, (h, i, err)
+
+
 # ------------------------------------------------------------------------------------ in-loop skip variant
 def _inloop_vs_list(p, x, dev, mask_dev=None):
     """Run bsa_prefill and bsa_prefill_inloop on the same mask (the GPU's own selection by default);
