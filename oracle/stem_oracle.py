@@ -44,7 +44,7 @@ __all__ = [
     "pool_blocks", "value_log_magnitude", "oam_block_scores", "oam_token_scores",
     "tpd_total", "tpd_solve", "tpd_budgets", "select_row", "select_all",
     "attention_rows", "block_sparse_attention", "dense_causal_attention", "causal_pairs",
-    "sampled_query_positions", "naive_block_scores",
+    "sampled_query_positions", "naive_block_scores", "e4m3fn_encode", "quantize_fp8_per_head",
 ]
 
 
@@ -78,6 +78,38 @@ def e4m3fn_table() -> np.ndarray:
 
 
 _E4M3 = e4m3fn_table()
+
+
+def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
+    """Real values (|y| <= 448) -> OCP e4m3fn codes, rounding to the nearest representable value, ties to
+    the even code.  Picks, for each value, the nearest entry of the definition table (positive codes
+    0x00..0x7E), preferring the even code on a tie."""
+    y = np.asarray(y, dtype=np.float64)
+    tab = e4m3fn_table()[:0x7F]  # non-negative finite values, increasing with the code
+    a = np.abs(y)
+    idx = np.searchsorted(tab, a)  # first code with value >= a
+    idx = np.clip(idx, 1, 0x7E)
+    lo, hi = tab[idx - 1], tab[idx]
+    pick_hi = (hi - a < a - lo) | ((hi - a == a - lo) & (idx % 2 == 0))
+    code = np.where(a >= tab[0x7E], 0x7E, np.where(a <= 0, 0, np.where(pick_hi, idx, idx - 1)))
+    return (code.astype(np.uint8) | (np.signbit(y).astype(np.uint8) << np.uint8(7))).astype(np.uint8)
+
+
+def quantize_fp8_per_head(x: np.ndarray):
+    """W8A8 quantisation of one tensor x [T][H][d] (values exactly representable in fp32), reading R10:
+    scale_h = fp32(amax_h / 448) (1 when amax_h = 0), y = fp32(x / scale_h) clamped to +-448, code =
+    e4m3fn round-to-nearest-even of y.  Returns (codes uint8 [T][H][d], scale float32 [H])."""
+    x = np.asarray(x, dtype=np.float64)
+    H = x.shape[1]
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scale = np.empty(H, dtype=np.float32)
+    for h in range(H):
+        amax = np.float32(np.abs(x[:, h]).max())
+        s = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+        scale[h] = s
+        y = (x[:, h].astype(np.float32) / s).astype(np.float32).astype(np.float64)
+        codes[:, h] = e4m3fn_encode(np.clip(y, -448.0, 448.0))
+    return codes, scale
 
 
 def fp8_to_f64(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:

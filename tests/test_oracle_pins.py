@@ -364,3 +364,36 @@ def test_naive_scores_against_masked_softmax_over_the_full_matrix():
         for i in range(n):
             want = np.log(mass[pos[i]].mean(axis=0)[: i + 1]) + 0.5 * M[g, : i + 1]
             assert np.max(np.abs(got[h, i, : i + 1] - want)) < 1e-12
+
+
+# ------------------------------------------------------------------------------------ W8A8 quantisation
+def test_e4m3fn_encoder_matches_torch_cast_including_midpoints():
+    rng = np.random.default_rng(0)
+    tab = oracle.e4m3fn_table()[:0x7F]
+    mids = ((tab[1:] + tab[:-1]) / 2).astype(np.float32)
+    y = np.concatenate([rng.uniform(-448, 448, 50000).astype(np.float32), rng.normal(0, 0.01, 5000).astype(np.float32),
+                        mids, -mids, tab.astype(np.float32), np.float32([0.0, -0.0, 448.0, -448.0])])
+    got = oracle.e4m3fn_encode(y.astype(np.float64))
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_quantize_fp8_per_head_closed_forms():
+    """amax maps to the largest code (448); the scale is amax/448 in fp32; half the amax maps to 224
+    (representable); decoding the codes times the scale stays within half a quantum of x."""
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(64, 3, 16)).astype(np.float32).astype(np.float64)
+    x[7, 1, 3] = 12.5  # head 1's amax
+    x[9, 1, 4] = -6.25  # half of it, negative
+    codes, scale = oracle.quantize_fp8_per_head(x)
+    assert scale[1] == np.float32(np.float32(12.5) / np.float32(448.0))
+    assert codes[7, 1, 3] == 0x7E and codes[9, 1, 4] == (0x80 | 0x76)  # 448 = 1.75*2^8, 224 = 1.75*2^7
+    back = oracle.fp8_to_f64(codes, scale)
+    tab = oracle.e4m3fn_table()
+    for h in range(3):
+        y = x[:, h] / float(scale[h])
+        q = tab[codes[:, h] & 0x7F]
+        e = np.maximum(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))), -6).astype(np.int64)
+        spacing = np.ldexp(1.0, np.minimum(e, 8) - 3)
+        assert np.all(np.abs(np.abs(y) - q) <= spacing / 2 + 1e-12)
+    assert np.all(np.isfinite(back))
