@@ -232,6 +232,43 @@ def measure_naive(L, q, k, v, p, dev, torch, score_ms, fused_ms, samples=4):
             "jaccard_with_pooled_selection": stats["jaccard_vs_default"]}
 
 
+def measure_quantize(dev, torch, reps):
+    """The 128K fp8 layer's stage 1 from bf16 activations: stem_quantize_score (amax, quantise + pool,
+    score) against stem_score on already-quantised inputs, and the bytes each moves."""
+    import synth
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    pb = synth.make_problem("w8a8_128k_fp8", dtype="bf16")
+    xb = synth.make_inputs(pb, seed=0)
+    q, k, v = upload(xb["q"]), upload(xb["k"]), upload(xb["v"])
+    q8, k8, v8 = (torch.empty(t.shape, dtype=torch.uint8, device=dev) for t in (q, k, v))
+    qs = torch.empty(pb.hq, dtype=torch.float32, device=dev)
+    ks = torch.empty(pb.hkv, dtype=torch.float32, device=dev)
+    vs = torch.empty(pb.hkv, dtype=torch.float32, device=dev)
+    prob = stem.make_problem(pb.cu_seqlens, pb.hq, pb.hkv, pb.d, pb.block, "fp8", q_scale=qs, k_scale=ks, v_scale=vs)
+    L = StemPrefill(prob, dev)
+
+    def run(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_fused = run(lambda: stem.stem_quantize_score(prob, q, k, v, q8, k8, v8, qs, ks, vs, pb.beta, L.scores, L.ws))
+    t_score = run(lambda: L.score(q8, k8, v8, pb.beta))
+    bf16_bytes = int(sum(t.numel() * 2 for t in (q, k, v)))
+    return {"workload": "w8a8_128k_fp8 from bf16 activations", "quantize_score_ms": round(t_fused, 4),
+            "score_on_fp8_ms": round(t_score, 4), "bf16_bytes_read_twice": bf16_bytes,
+            "fp8_bytes_written": bf16_bytes // 2,
+            "note": "a separate quantiser would read bf16 twice and write fp8, then stem_score reads the fp8 again"}
+
+
 def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
     """The oracle, as it stands, on a bounded sample of rows of the same workload: for each sampled
     (query head, query block) row it pools, scores, takes the TPD budget, selects and attends.
@@ -411,6 +448,9 @@ def main():
             log("[bench] ablation switches (mu = 1, beta = 0, beta/mu sweep)")
             out["ablations"] = measure_ablations(L, q, k, v, p, torch)
         if args.workload == "llama_128k_bf16" and not args.no_other_workloads:
+            log("[bench] W8A8 stage 1 from bf16 activations (quantisation fused with pooling)")
+            out["w8a8_quantize_score"] = measure_quantize(dev, torch, args.steps)
+            torch.cuda.empty_cache()
             others = {}
             for name in ("llama_32k_bf16", "w8a8_128k_fp8", "paged_ragged_bf16", "tiny_f32"):
                 log(f"[bench] other workload {name}")

@@ -3,5 +3,5 @@ selection and block-sparse flash attention, as a C-ABI library (libstem.so) with
 from ._abi import (  # noqa: F401
     DTYPES, EXPORTS, LIB_PATH, Problem, StemError, block_counts, bsa_prefill, lib, make_problem,
     stem_score, stem_score_select, stem_tpd_budgets_host, stem_tpd_topk, workspace_bytes, workspace_layout,
-    bsa_prefill_inloop,
+    bsa_prefill_inloop, stem_quantize_score, stem_naive_score, naive_workspace_bytes,
 )

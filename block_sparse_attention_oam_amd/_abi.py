@@ -26,7 +26,8 @@ MAX_REQS = 256
 
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
            "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
-           "bsa_prefill_inloop", "stem_score_select", "stem_naive_workspace_bytes", "stem_naive_score"]
+           "bsa_prefill_inloop", "stem_score_select", "stem_naive_workspace_bytes", "stem_naive_score",
+           "stem_quantize_score"]
 
 
 class StemError(RuntimeError):
@@ -82,11 +83,12 @@ def lib() -> ctypes.CDLL:
         L.bsa_prefill.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.stem_score_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
+        L.stem_quantize_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, i64, vp, sz, vp]
         L.stem_naive_workspace_bytes.argtypes = [P, i32]
         L.stem_naive_workspace_bytes.restype = sz
         L.stem_naive_score.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, vp, i64, vp, sz, vp, sz, vp]
         for name in ("stem_block_counts", "stem_workspace_layout", "stem_tpd_budgets_host", "stem_score",
-                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select", "stem_naive_score"):
+                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select", "stem_naive_score", "stem_quantize_score"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -199,6 +201,15 @@ def stem_score_select(p: Problem, q, k, v, beta: float, rho: tuple, mu: tuple, m
     _check(lib().stem_score_select(p.ref, _ptr(q), _ptr(k), _ptr(v), float(beta), int(rho[0]), int(rho[1]),
                                    int(mu[0]), int(mu[1]), _ptr(mask), words, _ptr(counts), _ptr(ws), ws_bytes,
                                    _stream(stream)))
+
+
+def stem_quantize_score(p: Problem, q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, beta: float, scores, ws,
+                        stream=None) -> None:
+    """bf16 q, k, v -> e4m3fn codes and per-head scales, pooled workspace and block scores (fp8 layer)."""
+    _check(lib().stem_quantize_score(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+                                     _ptr(k_scale), _ptr(v_scale), float(beta), _ptr(scores),
+                                     int(scores.shape[-1]) if scores is not None else 0, _ptr(ws),
+                                     int(ws.numel() * ws.element_size()) if ws is not None else 0, _stream(stream)))
 
 
 def naive_workspace_bytes(p: Problem, samples: int) -> int:

@@ -42,8 +42,29 @@ __device__ __forceinline__ void decode16(const uint4 w, float* x) {
   }
 }
 
-template <int EB>
+// Sixteen bf16 values (32 bytes) -> per-head-scaled e4m3fn codes (RNE, saturated at +-448), packed.
+__device__ __forceinline__ uint4 quant16(const uint4 w0, const uint4 w1, float s) {
+  float x[16];
+  decode16<2>(w0, x);
+  decode16<2>(w1, x + 8);
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * i + e] / s, -448.f), 448.f);
+    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    wv = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wv, true);
+    c[i] = (uint32_t)wv;
+  }
+  return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
+// QUANT: the inputs are bf16; each lane reads the 16 values that an fp8 lane would, quantises them with its
+// head's scale, stores the codes and pools the decoded codes exactly as the fp8 pool does.
+template <int EB, bool QUANT = false>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
+  static_assert(!QUANT || EB == 1, "quantising pool uses the fp8 lane layout");
   constexpr int EPL = 16 / EB;  // elements per lane
   const int ib = blockIdx.x;
   int job = blockIdx.y;
@@ -92,18 +113,35 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     if (EB == 1 && kind == 2) vscale = a.v_scale[head];
   }
 
-  auto row_ptr = [&](int t) -> const uint4* {
-    int64_t off;
-    if (kind == 0) off = (int64_t)(tb + t) * a.hq * d + e0;
-    else off = a.kv.row(r, tb, t, head) + dd;
-    return (const uint4*)(base + off * EB);
+  auto elem_off = [&](int t) -> int64_t {
+    if (kind == 0) return (int64_t)(tb + t) * a.hq * d + e0;
+    return a.kv.row(r, tb, t, head) + dd;
+  };
+  auto row_ptr = [&](int t) -> const uint4* { return (const uint4*)(base + elem_off(t) * EB); };
+  float qscale = 1.f;  // quantising pool: this lane's head scale
+  uint8_t* qdst = nullptr;
+  if constexpr (QUANT) {
+    qscale = kind == 0 ? a.q_scale[head] : (kind == 1 ? a.k_scale[head] : a.v_scale[head]);
+    qdst = (uint8_t*)(kind == 0 ? a.q8 : (kind == 1 ? a.k8 : a.v8));
+  }
+  // 16 bytes of this lane's row t: the stored vector, or (quantising) the codes of its 32 bf16 bytes
+  auto load = [&](int t) -> uint4 {
+    if constexpr (QUANT) {
+      const int64_t off = elem_off(t);
+      const uint4* src = (const uint4*)(base + off * 2);
+      const uint4 c = quant16(src[0], src[1], qscale);
+      *(uint4*)(qdst + off) = c;
+      return c;
+    } else {
+      return *row_ptr(t);
+    }
   };
 
   if (active) {
     if (kind != 2) {
       int t = t0 + rs;
       for (; t + 3 * tr < t1; t += 4 * tr) {
-        uint4 w0 = *row_ptr(t), w1 = *row_ptr(t + tr), w2 = *row_ptr(t + 2 * tr), w3 = *row_ptr(t + 3 * tr);
+        uint4 w0 = load(t), w1 = load(t + tr), w2 = load(t + 2 * tr), w3 = load(t + 3 * tr);
         float x[EPL];
         decode16<EB>(w0, x);
 #pragma unroll
@@ -120,7 +158,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
       }
       for (; t < t1; t += tr) {
         float x[EPL];
-        decode16<EB>(*row_ptr(t), x);
+        decode16<EB>(load(t), x);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] += x[e];
       }
@@ -132,7 +170,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
       float ss = 0.f;
       if (active && t < t1) {
         float x[EPL];
-        decode16<EB>(*row_ptr(t), x);
+        decode16<EB>(load(t), x);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           const float y = x[e] * vscale;
@@ -182,6 +220,50 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     float4 o = make_float4(acc[e] * sc, acc[e + 1] * sc, acc[e + 2] * sc, acc[e + 3] * sc);
     *(float4*)(dst + e) = o;
   }
+}
+
+// Per-head amax of bf16 Q, K, V (for the W8A8 scales): blockIdx.y selects the tensor, blockIdx.x a range of
+// 64 tokens; lanes of one head reduce by shuffles, one atomicMax per head and workgroup on the float bits
+// (non-negative floats order like their bit patterns).  amax[] must start at 0.
+__global__ __launch_bounds__(256) void amax_kernel(PoolArgs a, unsigned* qmax, unsigned* kmax, unsigned* vmax,
+                                                   int64_t tokens) {
+  const int kind = blockIdx.y;
+  const int H = kind == 0 ? a.hq : a.hkv;
+  const int rowlen = H * a.d;            // elements per token row
+  const int lanes = rowlen / 8;          // 16-byte vectors per row
+  const int hl = a.d / 8;                // lanes per head (16 or 8)
+  const uint16_t* src = (const uint16_t*)(kind == 0 ? a.q : (kind == 1 ? a.k : a.v));
+  unsigned* out = kind == 0 ? qmax : (kind == 1 ? kmax : vmax);
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  for (int c0 = 0; c0 < lanes; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    const bool ok = c < lanes;
+    float m = 0.f;
+    if (ok) {
+      for (int64_t t = t0; t < t0 + 64 && t < tokens; ++t) {
+        float x[8];
+        decode16<2>(*(const uint4*)(src + t * rowlen + (int64_t)c * 8), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+      }
+    }
+    for (int o = 1; o < hl; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (ok && (c % hl) == 0) atomicMax(out + c / hl, __float_as_uint(m));
+  }
+}
+
+// amax bits -> scale = amax / 448 (1 when amax is 0), in place.
+__global__ void scale_kernel(float* s, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float amax = __uint_as_float(__float_as_uint(s[i]));
+    s[i] = amax > 0.f ? amax / 448.f : 1.f;
+  }
+}
+
+__global__ void zero_kernel(float* s, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) s[i] = 0.f;
 }
 
 constexpr int kTile = 64;
@@ -259,6 +341,25 @@ hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s) {
   if (dtype == STEM_F32) hipLaunchKernelGGL(pool_kernel<4>, grid, dim3(kPoolThreads), 0, s, a);
   else if (dtype == STEM_BF16) hipLaunchKernelGGL(pool_kernel<2>, grid, dim3(kPoolThreads), 0, s, a);
   else hipLaunchKernelGGL(pool_kernel<1>, grid, dim3(kPoolThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pool(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((a.hq + 255) / 256)), dim3(256), 0, s, q_scale, a.hq);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, k_scale, a.hkv);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, v_scale, a.hkv);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)((tokens + 63) / 64), 3), dim3(256), 0, s, a, (unsigned*)q_scale,
+                     (unsigned*)k_scale, (unsigned*)v_scale, tokens);
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((a.hq + 255) / 256)), dim3(256), 0, s, q_scale, a.hq);
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, k_scale, a.hkv);
+  hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, v_scale, a.hkv);
+  PoolArgs b = a;
+  b.q_scale = q_scale;
+  b.k_scale = k_scale;
+  b.v_scale = v_scale;
+  dim3 grid((unsigned)a.NB, (unsigned)(a.q_chunks + 2 * a.kv_chunks));
+  hipLaunchKernelGGL((pool_kernel<1, true>), grid, dim3(kPoolThreads), 0, s, b);
   return hipGetLastError();
 }
 

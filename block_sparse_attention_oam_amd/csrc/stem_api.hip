@@ -294,6 +294,67 @@ int stem_score(const stem_problem* p, const void* q, const void* k, const void* 
   return hip_status(e, "score launch");
 }
 
+int stem_quantize_score(const stem_problem* p, const void* q, const void* k, const void* v, void* q8, void* k8,
+                        void* v8, float* q_scale, float* k_scale, float* v_scale, float beta, float* scores,
+                        int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  if (p->dtype != STEM_FP8_E4M3 || p->kv_paged)
+    return fail(STEM_E_UNSUPPORTED, "quantising scoring describes an fp8 layer with contiguous K/V");
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !scores)
+    return fail(STEM_E_INVALID_ARG, "q8, k8, v8, the scale arrays and scores must be non-NULL");
+  if (score_row_stride < pl.max_n)
+    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d", (long long)score_row_stride, pl.max_n);
+  st = check_pool_args(p, pl, q, k, v, beta, ws, ws_bytes);
+  if (st != STEM_OK) return st;
+  if (((uintptr_t)q8 | (uintptr_t)k8 | (uintptr_t)v8) & 15)
+    return fail(STEM_E_INVALID_ARG, "q8, k8 and v8 must be 16-byte aligned");
+  st = check_device();
+  if (st != STEM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  size_t oq, okk, om, need;
+  layout(pl, &oq, &okk, &om, &need);
+  PoolArgs pa;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.q8 = q8;
+  pa.k8 = k8;
+  pa.v8 = v8;
+  pa.qbar = (float*)((char*)ws + oq);
+  pa.kbar = (float*)((char*)ws + okk);
+  pa.M = (float*)((char*)ws + om);
+  pa.q_scale = q_scale;
+  pa.k_scale = k_scale;
+  pa.v_scale = v_scale;
+  pa.hq = p->hq;
+  pa.hkv = p->hkv;
+  pa.d = p->head_dim;
+  pa.B = p->block;
+  pa.NB = pl.NB;
+  pa.q_chunks = (p->hq * p->head_dim / 16 + 255) / 256;  // fp8 lane layout: 16 elements per lane
+  pa.kv_chunks = (p->hkv * p->head_dim / 16 + 255) / 256;
+  pa.kv = pl.kv;
+  pa.rt = pl.rt;
+  hipError_t e = launch_quant_pool(pa, q_scale, k_scale, v_scale, pl.tokens, s);
+  if (e != hipSuccess) return hip_status(e, "quantising pool launch");
+  ScoreArgs sa;
+  sa.qbar = pa.qbar;
+  sa.kbar = pa.kbar;
+  sa.M = pa.M;
+  sa.scores = scores;
+  sa.stride = score_row_stride;
+  sa.NB = pl.NB;
+  sa.hq = p->hq;
+  sa.hkv = p->hkv;
+  sa.d = p->head_dim;
+  sa.beta = beta;
+  sa.inv_sqrt_d = 1.0f / sqrtf((float)p->head_dim);
+  sa.rt = pl.rt;
+  return hip_status(launch_score(sa, pl.max_n, p->num_reqs, s), "score launch");
+}
+
 // Budget and mask arguments shared by stem_tpd_topk and stem_score_select.
 static int check_select_args(const Plan& pl, int32_t rho_num, int32_t rho_den, int32_t mu_num, int32_t mu_den,
                              const uint32_t* mask, int32_t mask_row_words, const int32_t* counts) {

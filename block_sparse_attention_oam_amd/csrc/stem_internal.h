@@ -20,9 +20,12 @@ struct Plan {
 };
 
 struct PoolArgs {
-  const void* q;
+  const void* q;  // inputs (bf16 sources when quantising)
   const void* k;
   const void* v;
+  void* q8;       // quantising pool only: e4m3fn outputs in the same layouts
+  void* k8;
+  void* v8;
   float* qbar;
   float* kbar;
   float* M;
@@ -109,6 +112,9 @@ struct BsaArgs {
 };
 
 hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s);
+// bf16 inputs -> per-head amax into the scale arrays, scales, then the quantising pool (fp8 codes out).
+hipError_t launch_quant_pool(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
+                             hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_score_topk(const ScoreTopkArgs& a, int max_n, int num_reqs, hipStream_t s);

@@ -124,6 +124,20 @@ int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_
                   int32_t rho_den, int32_t mu_num, int32_t mu_den, uint32_t* mask, int32_t mask_row_words,
                   int32_t* counts, void* stream);
 
+/* Stage 1 for an fp8 (W8A8) layer from bf16 activations: quantisation fused with pooling -------------- */
+/* q, k, v: DEVICE bf16 in the layouts above (contiguous K/V).  Writes the per-head scales
+ * q_scale[hq], k_scale[hkv], v_scale[hkv] (DEVICE; scale = amax / 448 in fp32, 1 for an all-zero head),
+ * the e4m3fn codes q8, k8, v8 (DEVICE, same layouts; code = round-to-nearest-even of x / scale clamped to
+ * +-448), and then exactly what stem_score computes from those codes and scales (pooled workspace and
+ * block scores), without reading the codes back: the pooling works on the values it has just quantised.
+ * p describes the fp8 layer (dtype STEM_FP8_E4M3, contiguous K/V); its own scale pointers are not read
+ * here (they are normally these same output arrays, for the later stages).
+ * Source: "答案不在算法里" (W8A8-FP8 deployment) with "HPC-Stem：评估选块，快几十倍" (fusing to avoid passes
+ * through HBM). */
+int stem_quantize_score(const stem_problem* p, const void* q, const void* k, const void* v, void* q8, void* k8,
+                        void* v8, float* q_scale, float* k_scale, float* v_scale, float beta, float* scores,
+                        int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream);
+
 /* Stages 1 + 2 fused: the score tensor never reaches memory ---------------------------------------- */
 /* Pools Q/K/V into the workspace exactly as stem_score does, then computes each row's block scores on
  * chip and selects from them exactly as stem_tpd_topk does: mask and counts are bit-identical to

@@ -95,19 +95,21 @@ def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
     return (code.astype(np.uint8) | (np.signbit(y).astype(np.uint8) << np.uint8(7))).astype(np.uint8)
 
 
-def quantize_fp8_per_head(x: np.ndarray):
+def quantize_fp8_per_head(x: np.ndarray, rows=None):
     """W8A8 quantisation of one tensor x [T][H][d] (values exactly representable in fp32), reading R10:
     scale_h = fp32(amax_h / 448) (1 when amax_h = 0), y = fp32(x / scale_h) clamped to +-448, code =
-    e4m3fn round-to-nearest-even of y.  Returns (codes uint8 [T][H][d], scale float32 [H])."""
-    x = np.asarray(x, dtype=np.float64)
+    e4m3fn round-to-nearest-even of y.  Returns (codes uint8 [T][H][d], scale float32 [H]); with `rows`
+    (token indices) the scales still come from all of x but only those rows are encoded ([len][H][d])."""
+    x = np.asarray(x)
     H = x.shape[1]
-    codes = np.empty(x.shape, dtype=np.uint8)
+    sel = x if rows is None else x[rows]
+    codes = np.empty(sel.shape, dtype=np.uint8)
     scale = np.empty(H, dtype=np.float32)
     for h in range(H):
         amax = np.float32(np.abs(x[:, h]).max())
         s = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
         scale[h] = s
-        y = (x[:, h].astype(np.float32) / s).astype(np.float32).astype(np.float64)
+        y = (sel[:, h].astype(np.float32) / s).astype(np.float32).astype(np.float64)
         codes[:, h] = e4m3fn_encode(np.clip(y, -448.0, 448.0))
     return codes, scale
 

@@ -227,6 +227,75 @@ def test_full_size_workload(dev, name):
     assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
 
 
+# ------------------------------------------------------------------------------------ W8A8 quantising stage 1
+def _quantize_and_reference(p8, xb, dev):
+    """stem_quantize_score on bf16 inputs, and stem_score on the codes and scales it produced."""
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    q, k, v = upload(xb["q"]), upload(xb["k"]), upload(xb["v"])
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    v8 = torch.empty(v.shape, dtype=torch.uint8, device=dev)
+    qs = torch.empty(p8.hq, dtype=torch.float32, device=dev)
+    ks = torch.empty(p8.hkv, dtype=torch.float32, device=dev)
+    vs = torch.empty(p8.hkv, dtype=torch.float32, device=dev)
+    prob = stem.make_problem(p8.cu_seqlens, p8.hq, p8.hkv, p8.d, p8.block, "fp8", q_scale=qs, k_scale=ks, v_scale=vs)
+    L1 = StemPrefill(prob, dev)
+    L1.scores.fill_(float("nan"))
+    stem.stem_quantize_score(prob, q, k, v, q8, k8, v8, qs, ks, vs, p8.beta, L1.scores, L1.ws)
+    L2 = StemPrefill(prob, dev)
+    L2.scores.fill_(float("nan"))
+    L2.score(q8, k8, v8, p8.beta)
+    torch.cuda.synchronize()
+    return L1, L2, (q8, k8, v8), (qs, ks, vs)
+
+
+@pytest.mark.parametrize("over", [dict(lens=(1000,), hq=8, hkv=2), dict(lens=(200, 513), hq=4, hkv=1, d=64),
+                                  dict(lens=(2000, 300), hq=8, hkv=8, block=64)])
+def test_quantize_score_codes_scales_and_pooling(dev, over):
+    """Codes and scales bit-exact against the oracle's quantisation; pooled tensors and scores bit-exact
+    against stem_score run on those codes."""
+    pb = synth.make_problem("w8a8_128k_fp8", dtype="bf16", **over)
+    p8 = synth.make_problem("w8a8_128k_fp8", **over)
+    xb = synth.make_inputs(pb, seed=4)
+    L1, L2, codes, scales = _quantize_and_reference(p8, xb, dev)
+    for name, c, s_ in (("q", codes[0], scales[0]), ("k", codes[1], scales[1]), ("v", codes[2], scales[2])):
+        want_c, want_s = oracle.quantize_fp8_per_head(oracle.bf16_to_f64(xb[name]))
+        assert np.array_equal(s_.cpu().numpy(), want_s), name
+        assert np.array_equal(c.cpu().numpy(), want_c), name
+    for t1, t2 in zip(L1.pooled(), L2.pooled()):
+        assert torch.equal(t1, t2)
+    n = max(p8.nblocks(r) for r in range(len(p8.lens)))
+    tri = torch.tril(torch.ones(n, n, dtype=torch.bool, device=dev))
+    for r in range(len(p8.lens)):
+        nr = p8.nblocks(r)
+        a = L1.scores[:, p8.cu_blocks[r]:p8.cu_blocks[r + 1], :nr][:, tri[:nr, :nr]]
+        b = L2.scores[:, p8.cu_blocks[r]:p8.cu_blocks[r + 1], :nr][:, tri[:nr, :nr]]
+        assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(600)
+def test_quantize_score_full_size_128k(dev):
+    """The 128K fp8 layer from its bf16 activations: scales bit-exact, codes bit-exact on sampled token
+    rows, pooled tensors and scores bit-exact against stem_score on the produced codes."""
+    pb = synth.make_problem("w8a8_128k_fp8", dtype="bf16")
+    p8 = synth.make_problem("w8a8_128k_fp8")
+    _log("[quant] 128K: generating bf16 inputs")
+    xb = synth.make_inputs(pb, seed=0)
+    L1, L2, codes, scales = _quantize_and_reference(p8, xb, dev)
+    rows = np.random.default_rng(0).choice(p8.tokens, 512, replace=False)
+    for name, c, s_ in (("q", codes[0], scales[0]), ("k", codes[1], scales[1]), ("v", codes[2], scales[2])):
+        want_c, want_s = oracle.quantize_fp8_per_head(oracle.bf16_to_f64(xb[name]), rows=rows)
+        assert np.array_equal(s_.cpu().numpy(), want_s), name
+        assert np.array_equal(c.cpu().numpy()[rows], want_c), name
+    for t1, t2 in zip(L1.pooled(), L2.pooled()):
+        assert torch.equal(t1, t2)
+    n = p8.nblocks(0)
+    tri = torch.tril(torch.ones(n, n, dtype=torch.bool, device=dev))
+    assert torch.equal(L1.scores[:, :, :n][:, tri], L2.scores[:, :, :n][:, tri])
+
+
 # ------------------------------------------------------------------------------------ fused scoring + selection
 def _fused_vs_two_stage(p, x, dev):
     """Masks and counts from stem_score + stem_tpd_topk and from stem_score_select on the same inputs."""
