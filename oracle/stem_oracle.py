@@ -159,6 +159,8 @@ def pool_blocks(x: np.ndarray, B: int) -> np.ndarray:
     can be replaced by per-block compact representations of Q and K and one GEMM.
     """
     L = x.shape[0]
+    if L == 0:  # a request with no tokens has no blocks
+        return np.zeros((x.shape[1], 0, x.shape[2]))
     out = np.stack([x[a:b].mean(axis=0) for a, b in _blocks(L, B)], axis=1)  # [H][n][d]
     return out
 
@@ -169,6 +171,8 @@ def value_log_magnitude(v: np.ndarray, B: int) -> np.ndarray:
     [Arch] "OAM": the score adds the signal magnitude log||V_j||_2 to the routing relevance.
     """
     L = v.shape[0]
+    if L == 0:
+        return np.zeros((v.shape[1], 0))
     lognorm = np.log(np.sqrt(np.sum(v * v, axis=-1)))  # [L][H]
     return np.stack([lognorm[a:b].mean(axis=0) for a, b in _blocks(L, B)], axis=1)  # [H][n]
 
@@ -275,8 +279,11 @@ def tpd_solve(n: int, T: int, mu: Fraction):
 def tpd_budgets(n: int, rho_num: int, rho_den: int, mu_num: int, mu_den: int) -> np.ndarray:
     """Integer per-row budgets k_i (reading R7): k_i = K_i - K_{i-1}, K_i = floor(P_i + 1/2), P_i = sum r.
 
-    Rounding the prefix sums keeps sum_i k_i = T exactly and |k_i - r_i| < 1.
+    Rounding the prefix sums keeps sum_i k_i = T exactly and |k_i - r_i| < 1.  A request with no tokens has
+    no rows (empty result).
     """
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
     T = tpd_total(n, rho_num, rho_den)
     _, rs = tpd_solve(n, T, Fraction(mu_num, mu_den))
     k = np.empty(n, dtype=np.int64)

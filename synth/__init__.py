@@ -129,6 +129,8 @@ def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
 
 def _ar1(innov: np.ndarray, phi: float) -> np.ndarray:
     """AR(1) along axis 0 with unit stationary variance: z_0 = e_0, z_t = phi z_{t-1} + sqrt(1-phi^2) e_t."""
+    if innov.shape[0] == 0:  # an empty request
+        return innov.astype(np.float64)
     c = math.sqrt(1.0 - phi * phi)
     z = lfilter([c], [1.0, -phi], innov.astype(np.float64), axis=0)
     # lfilter's first output is c*e_0; rescale the start so z_0 = e_0 (stationary start), then propagate.

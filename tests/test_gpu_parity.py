@@ -84,6 +84,8 @@ def _check_stage1(p, g, ref):
     cb = p.cu_blocks
     worst_s = 0.0
     for r, (qbar, kbar, M, S) in enumerate(ref):
+        if S.shape[1] == 0:  # an empty request: no blocks
+            continue
         sl = slice(cb[r], cb[r + 1])
         assert np.max(np.abs(g["qbar"][:, sl] - qbar)) < 1e-5
         assert np.max(np.abs(g["kbar"][:, sl] - kbar)) < 1e-5
@@ -112,6 +114,9 @@ SMALL = [
     ("paged_ragged_bf16", dict(lens=(300, 64, 700), hq=4, hkv=2)),
     ("paged_ragged_bf16", dict(lens=(257, 1000), hq=4, hkv=1, page_size=16)),
     ("paged_ragged_bf16", dict(lens=(129, 500), hq=2, hkv=2, page_size=32, dtype="fp8")),
+    ("llama_32k_bf16", dict(lens=(300, 0, 129), hq=4, hkv=2)),  # an empty request inside a batch
+    ("paged_ragged_bf16", dict(lens=(0, 200, 0, 64), hq=2, hkv=1)),
+    ("w8a8_128k_fp8", dict(lens=(0, 700), hq=4, hkv=2)),
 ]
 
 
@@ -512,6 +517,31 @@ def test_ablation_switches_full_size_32k(dev, over):
     _log(f"  score rel {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
     tmax, tmean = sc.TOL[p.dtype]
     assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+
+
+# ------------------------------------------------------------------------------------ maximum sizes
+@pytest.mark.timeout(900)
+def test_longest_request_the_masked_kernels_take(dev):
+    """2048 blocks in one request (262144 tokens, the masked attention kernels' limit), 2 query heads: every
+    budget and selection against the oracle, attention on sampled rows, and the fused selection equal to
+    the two-stage one."""
+    p = synth.make_problem("llama_128k_bf16", lens=(2048 * 128,), hq=2, hkv=1)
+    _log("[max] 2048 blocks: generating inputs")
+    x = synth.make_inputs(p, seed=6)
+    ref1 = sc.oracle_stage1(p, x)
+    S_list = [s for *_, s in ref1]
+    budgets = sc.oracle_budgets(p)
+    masks = sc.oracle_masks(S_list, budgets)
+    g = _run(p, x, dev, masks_for_bsa=masks)
+    _check_stage1(p, g, ref1)
+    ties = sc.check_selection(p, S_list, budgets, g["words"], g["counts"])
+    rows = [sc.sample_rows(p, 0, 6)]
+    ora = sc.oracle_attention(p, x, masks, rows)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
+    _log(f"[max] near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
+    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= 0.2
+    L, m1, c1 = _fused_vs_two_stage(p, x, dev)
+    assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
 
 
 # ------------------------------------------------------------------------------------ budgets on the device
