@@ -269,6 +269,26 @@ def measure_quantize(dev, torch, reps):
             "note": "a separate quantiser would read bf16 twice and write fp8, then stem_score reads the fp8 again"}
 
 
+def measure_cold(L, q, k, v, p, torch, dev, steps=7):
+    """Layer time with the caches evicted before every step (a 1 GiB buffer is overwritten between
+    steps, outside the timed events): median, p10 and p90 over the steps."""
+    rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(steps):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.forward(q, k, v, p.beta, rho, mu)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del scratch
+    t = np.array(times)
+    return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4), "steps": steps}
+
+
 def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
     """The oracle, as it stands, on a bounded sample of rows of the same workload: for each sampled
     (query head, query block) row it pools, scores, takes the TPD budget, selects and attends.
@@ -401,6 +421,8 @@ def main():
                        "unit": "TFLOP/s", "frac": round(bsa_tflops / peak, 4),
                        "traffic": traffic_from_profile(sha), "avg_launch_ms": round(bsa_ms, 4)}
     if not args.no_extras:
+        log("[bench] cold steps (1 GiB written between steps to evict L2 and MALL)")
+        out["cold_layer_ms"] = measure_cold(L, q, k, v, p, torch, dev)
         log("[bench] fused scoring + selection")
         rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
         ref_mask = L.mask.clone()
