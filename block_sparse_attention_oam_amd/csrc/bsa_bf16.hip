@@ -29,6 +29,11 @@
 //    instructions; rows past the request's end fall outside the buffer and read as zeros.  Small pages
 //    look up one page per row.  The diagonal block takes a separate path with the causal mask; other
 //    blocks have no per-element compares.
+//  * HEADS = 2 (an even number of query heads per KV head): one workgroup of 8 waves serves the same query
+//    block of two query heads of a KV group (waves 0-3 the first, 4-7 the second), so every K/V sub-tile it
+//    loads feeds twice the MFMA work and each wave issues half the loads.  The list is the union of the
+//    two mask rows, each entry carrying one selection bit per head; a wave skips the compute of a block its
+//    head did not select (the heads of a KV group select nearly the same blocks).
 #include "stem_internal.h"
 
 namespace stem {
@@ -38,9 +43,12 @@ namespace {
 constexpr int D = 128;
 constexpr int B = 128;
 constexpr int KT = 64;
-constexpr int NT = 256;
 constexpr int TILE = KT * D * 2;  // bytes per K or V sub-tile
 constexpr int kMaxList = 2048;
+// List entries: block index in the low bits, one selection bit per head of the workgroup.
+constexpr uint32_t kBlockBits = 0x3FFF;
+constexpr uint32_t kSelFirst = 0x4000;
+constexpr uint32_t kSelSecond = 0x8000;
 // Softmax reference point: the reference max m_run (log2 units) is set from the first visible keys of a
 // row and then kept while the tile sums of P = 2^(s - m_run) stay <= 2^32 (no overflow anywhere in P,
 // the row sum or O^T); a larger sum rebases to the tile's max.  P keeps bf16's relative precision at any
@@ -69,12 +77,13 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 // loop walks every causal block j <= i and tests j's mask bit (kept in LDS) at each step, skipping the
 // compute and the loads of unselected blocks but not the step itself (its barrier and bookkeeping).
 // Selected blocks see exactly the same arithmetic in the same order, so the outputs are identical.
-template <int PAGE, bool MASKED, bool INLOOP = false>
-__global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
+template <int PAGE, bool MASKED, bool INLOOP, int HEADS>
+__global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArgs a) {
+  constexpr int PARTS = 4 / HEADS;  // 1 KB load instructions per wave for each of K and V per sub-tile
   // Two buffers, each its own LDS object, so the loads into one are known not to alias reads of the other.
   __shared__ __align__(1024) uint8_t kbuf0[TILE], vbuf0[TILE], kbuf1[TILE], vbuf1[TILE];
   __shared__ uint16_t list[(MASKED && !INLOOP) ? kMaxList : 1];
-  __shared__ uint32_t mbits[INLOOP ? kMaxList / 32 : 1];
+  __shared__ uint32_t mbits[INLOOP ? HEADS * kMaxList / 32 : 1];
   __shared__ int list_len;
 
   const int tid = threadIdx.x;
@@ -82,49 +91,55 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  const int hsel = HEADS == 2 ? wave >> 2 : 0;  // head of the workgroup this wave serves
+  const int wq = HEADS == 2 ? wave & 3 : wave;   // 32-row slice of the query block
+  const uint32_t mine = hsel ? kSelSecond : kSelFirst;
 
-  // ---- work item (same order as the generic kernel: XCD-aware, KV-head-major, longest rows first)
+  // ---- work item (same order as the generic kernel: XCD-aware, KV-head-major, longest rows first);
+  //      HEADS consecutive query heads of one KV group per workgroup
   const int grp = a.hq / a.hkv;
+  const int hgroups = grp / HEADS;
   int64_t logical = blockIdx.x;
   if (a.xcd_remap) {
     const int64_t per = (int64_t)gridDim.x / 8;
     logical = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
   }
-  const int64_t per_g = a.NB * grp;
+  const int64_t per_g = a.NB * hgroups;
   const int g = (int)(logical / per_g);
   const int64_t rem = logical % per_g;
-  const int64_t ib = a.NB - 1 - rem / grp;
-  const int h = g * grp + (int)(rem % grp);
+  const int64_t ib = a.NB - 1 - rem / hgroups;
+  const int h0 = g * grp + HEADS * (int)(rem % hgroups);
+  const int h = h0 + hsel;
   const int r = find_request(a.rt, (int)ib);
   const int i = (int)ib - a.rt.cu_blocks[r];
   const int tb = a.rt.cu_seqlens[r];
   const int L = a.rt.cu_seqlens[r + 1] - tb;
+  // mask row of the workgroup's head t (rows of consecutive heads are NB * mask_words words apart)
+  auto mask_row = [&](int t) { return a.mask + ((int64_t)(h0 + t) * a.NB + ib) * a.mask_words; };
 
-  // ---- list of selected blocks
+  // ---- list of selected blocks (union over the workgroup's heads, one selection bit per head)
   int nsel;
   if constexpr (INLOOP) {
     if (wave == 0) {
-      const uint32_t* mrow = a.mask + ((int64_t)h * a.NB + ib) * a.mask_words;
       const int nwords = (i >> 5) + 1;
-      for (int w = lane; w < nwords; w += 64) mbits[w] = mrow[w];
+      for (int t = 0; t < HEADS; ++t)
+        for (int w = lane; w < nwords; w += 64) mbits[t * (kMaxList / 32) + w] = mask_row(t)[w];
     }
     __syncthreads();
     nsel = i + 1;
   } else if constexpr (MASKED) {
     if (wave == 0) {
-      const uint32_t* mrow = a.mask + ((int64_t)h * a.NB + ib) * a.mask_words;
       const int nwords = (i >> 5) + 1;
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += 64) {
         const int w = w0 + lane;
-        uint32_t word = 0;
+        uint32_t wa = 0, wb = 0;
         if (w < nwords) {
-          word = mrow[w];
-          if (w == nwords - 1) {
-            const int nb = (i & 31) + 1;
-            word &= (nb == 32) ? 0xFFFFFFFFu : ((1u << nb) - 1u);
-          }
+          const uint32_t keep = (w == nwords - 1 && (i & 31) != 31) ? ((1u << ((i & 31) + 1)) - 1u) : 0xFFFFFFFFu;
+          wa = mask_row(0)[w] & keep;
+          if (HEADS == 2) wb = mask_row(1)[w] & keep;
         }
+        uint32_t word = wa | wb;
         const int c = __popc(word);
         int incl = c;
         for (int o = 1; o < 64; o <<= 1) {
@@ -134,7 +149,8 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
         int pos = base + incl - c;
         while (word) {
           const int bit = __ffs(word) - 1;
-          list[pos++] = (uint16_t)(w * 32 + bit);
+          const uint32_t sel = (((wa >> bit) & 1u) ? kSelFirst : 0u) | (((wb >> bit) & 1u) ? kSelSecond : 0u);
+          list[pos++] = (uint16_t)((uint32_t)(w * 32 + bit) | sel);
           word &= word - 1;
         }
         base += __shfl(incl, 63, 64);
@@ -149,7 +165,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   const int nsub = nsel * 2;
 
   // ---- Q fragments (B operand of S^T = K Q^T)
-  const int qr = wave * 32 + l32;
+  const int qr = wq * 32 + l32;
   const int qpos = i * B + qr;
   const bool qvalid = qpos < L;
   bf16x8 qf[8];
@@ -162,17 +178,18 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     }
   }
 
-  // ---- loader geometry: instruction m of this wave fills LDS chunk (4*wave + m) = tile rows
-  //      16*wave + 4*m + lane/16, slot lane & 15 (16 bytes); the lane fetches the swizzled source chunk.
+  // ---- loader geometry: instruction m of this wave fills LDS chunk c = PARTS*wave + m = tile rows
+  //      4c + lane/16, slot lane & 15 (16 bytes); the lane fetches the swizzled source chunk.
   //      Contiguous K/V and pages of >= 64 tokens: buffer loads whose base (the sub-tile's first row) is
   //      scalar and whose per-lane byte offsets never change, with the buffer size ending at the
   //      request's last row (rows past it read as zeros; they are causally masked).  Smaller pages: one
   //      page lookup per row and global addresses.
   const int64_t row_stride = (int64_t)a.hkv * D * 2;
+  // (fixed size 4: lambdas that capture arrays of template-dependent size lose their host stubs)
   int ldrow[4], kchunk[4], vchunk[4], koff_ld[4], voff_ld[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int row = 16 * wave + 4 * m + (lane >> 4);
+  for (int m = 0; m < PARTS; ++m) {
+    const int row = 4 * (PARTS * wave + m) + (lane >> 4);
     const int slot = lane & 15;
     ldrow[m] = row;
     kchunk[m] = slot ^ (row & 15);
@@ -184,19 +201,23 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   const uint8_t* vbase_all = (const uint8_t*)a.v;
   const int64_t head_off = (int64_t)g * D * 2;
 
-  auto sub_key0 = [&](int u) -> int {
-    const int j = (MASKED && !INLOOP) ? (int)list[u >> 1] : (u >> 1);
-    return j * B + (u & 1) * KT;
-  };
-  // in-loop variant: is sub-tile u's block selected?
-  auto selected = [&](int u) -> bool {
-    if constexpr (INLOOP) {
+  // list entry of sub-tile u: block index | selection bits
+  auto entry = [&](int u) -> uint32_t {
+    if constexpr (MASKED && !INLOOP) {
+      return (uint32_t)list[u >> 1];
+    } else if constexpr (INLOOP) {
       const int j = u >> 1;
-      return (mbits[j >> 5] >> (j & 31)) & 1u;
+      uint32_t e = (uint32_t)j;
+      if ((mbits[j >> 5] >> (j & 31)) & 1u) e |= kSelFirst;
+      if (HEADS == 2 && ((mbits[kMaxList / 32 + (j >> 5)] >> (j & 31)) & 1u)) e |= kSelSecond;
+      return e;
     } else {
-      return true;
+      return (uint32_t)(u >> 1) | kSelFirst | kSelSecond;
     }
   };
+  auto sub_key0 = [&](uint32_t e, int u) -> int { return (int)(e & kBlockBits) * B + (u & 1) * KT; };
+  // must the workgroup load sub-tile u (in-loop variant: is its block selected by any head)?
+  auto wanted = [&](uint32_t e) -> bool { return !INLOOP || (e & (kSelFirst | kSelSecond)) != 0; };
 
   // The loads of sub-tile u: part m fills LDS chunk m of this wave in K and in V.  kb/vb: the sub-tile's
   // first row (scalar); nrec: bytes up to the request's end.
@@ -228,14 +249,16 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     return tok0 * row_stride + head_off;
   };
   auto issue_loads = [&](int u, uint8_t* kdst, uint8_t* vdst) {
-    const int kp0 = sub_key0(u);
-    if (kp0 >= L) return;  // a second half-block past the end of the request: nothing to load
+    const uint32_t e = entry(u);
+    const int kp0 = sub_key0(e, u);
+    // a second half-block past the end of the request, or (in-loop variant) a block nobody selected
+    if (kp0 >= L || !wanted(e)) return;
     const int64_t base = tile_base(kp0);
     const int nrec = min(L - kp0, KT) * (int)row_stride;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      issue_part(kp0, nrec, kbase_all + base, vbase_all + base, (lds_u8*)kdst + wave * 4096,
-                 (lds_u8*)vdst + wave * 4096, m);
+    for (int m = 0; m < PARTS; ++m)
+      issue_part(kp0, nrec, kbase_all + base, vbase_all + base, (lds_u8*)kdst + wave * (PARTS * 1024),
+                 (lds_u8*)vdst + wave * (PARTS * 1024), m);
   };
 
   // ---- operand read offsets (bytes inside a tile)
@@ -269,12 +292,13 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
   auto step = [&](int u, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (u + 1 < nsub && selected(u + 1)) issue_loads(u + 1, knext, vnext);
-    const int kp0 = sub_key0(u);
+    if (u + 1 < nsub) issue_loads(u + 1, knext, vnext);
+    const uint32_t e = entry(u);
+    const int kp0 = sub_key0(e, u);
     const bool diag = (kp0 / B) == i;
     // nothing to compute: the sub-tile starts past the request's end, or (diagonal block) every key is
-    // after the wave's rows, or (in-loop variant) its block is not selected
-    const bool idle = kp0 >= L || (diag && kp0 > i * B + wave * 32 + 31) || !selected(u);
+    // after the wave's rows, or the wave's head did not select the block
+    const bool idle = kp0 >= L || (diag && kp0 > i * B + wq * 32 + 31) || !(e & mine);
     if (idle) return;
     const lds_u8* Kt = (const lds_u8*)kcur;
     const lds_u8* Vt = (const lds_u8*)vcur;
@@ -386,7 +410,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_bf16_kernel(BsaArgs a) {
     }
   };
 
-  if (nsub > 0 && selected(0)) issue_loads(0, kbuf0, vbuf0);
+  if (nsub > 0) issue_loads(0, kbuf0, vbuf0);
   for (int u = 0; u < nsub; u += 2) {
     step(u, kbuf0, vbuf0, kbuf1, vbuf1);
     if (u + 1 < nsub) step(u + 1, kbuf1, vbuf1, kbuf0, vbuf0);
@@ -417,27 +441,30 @@ bool bsa_bf16_supported(int dtype, int head_dim, int block) {
   return dtype == STEM_BF16 && head_dim == D && block == B;
 }
 
-hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s) {
-  dim3 grid((unsigned)(a.hq * a.NB));
-  dim3 block(NT);
+template <bool MASKED, bool INLOOP, int HEADS>
+static hipError_t launch_heads(const BsaArgs& args, hipStream_t s) {
+  BsaArgs a = args;
+  const int64_t wgs = (int64_t)(a.hq / HEADS) * a.NB;
+  a.xcd_remap = wgs % 8 == 0 ? 1 : 0;
+  const dim3 grid((unsigned)wgs), block(256 * HEADS);
   const int page_mode = !a.kv.paged ? 0 : (a.kv.page_size % KT == 0 ? 1 : 2);
-#define STEM_LAUNCH(PM)                                                                     \
-  do {                                                                                      \
-    if (masked) hipLaunchKernelGGL((bsa_bf16_kernel<PM, true>), grid, block, 0, s, a);      \
-    else hipLaunchKernelGGL((bsa_bf16_kernel<PM, false>), grid, block, 0, s, a);            \
-  } while (0)
-  if (page_mode == 0) STEM_LAUNCH(0);
-  else if (page_mode == 1) STEM_LAUNCH(1);
-  else STEM_LAUNCH(2);
-#undef STEM_LAUNCH
+  if (INLOOP || page_mode == 0) hipLaunchKernelGGL((bsa_bf16_kernel<0, MASKED, INLOOP, HEADS>), grid, block, 0, s, a);
+  else if constexpr (!INLOOP) {  // the in-loop comparator takes contiguous K/V only
+    if (page_mode == 1) hipLaunchKernelGGL((bsa_bf16_kernel<1, MASKED, INLOOP, HEADS>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bsa_bf16_kernel<2, MASKED, INLOOP, HEADS>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
+// Two heads per workgroup whenever a KV group has an even number of query heads.
+hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s) {
+  const bool pair = (a.hq / a.hkv) % 2 == 0;
+  if (masked) return pair ? launch_heads<true, false, 2>(a, s) : launch_heads<true, false, 1>(a, s);
+  return pair ? launch_heads<false, false, 2>(a, s) : launch_heads<false, false, 1>(a, s);
+}
+
 hipError_t launch_bsa_bf16_inloop(const BsaArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.hq * a.NB));
-  dim3 block(NT);
-  hipLaunchKernelGGL((bsa_bf16_kernel<0, true, true>), grid, block, 0, s, a);
-  return hipGetLastError();
+  return (a.hq / a.hkv) % 2 == 0 ? launch_heads<true, true, 2>(a, s) : launch_heads<true, true, 1>(a, s);
 }
 
 }  // namespace stem

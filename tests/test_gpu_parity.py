@@ -117,6 +117,9 @@ SMALL = [
     ("llama_32k_bf16", dict(lens=(300, 0, 129), hq=4, hkv=2)),  # an empty request inside a batch
     ("paged_ragged_bf16", dict(lens=(0, 200, 0, 64), hq=2, hkv=1)),
     ("w8a8_128k_fp8", dict(lens=(0, 700), hq=4, hkv=2)),
+    # an odd number of query heads per KV head: one head per workgroup, with pages of 64 and of 16 tokens
+    ("paged_ragged_bf16", dict(lens=(300, 700), hq=3, hkv=1)),
+    ("paged_ragged_bf16", dict(lens=(257, 1000), hq=3, hkv=3, page_size=16)),
 ]
 
 
