@@ -5,16 +5,22 @@
 // on chip, the list of KV blocks, the dense inner loop over the list only; skipped blocks act as -inf
 // scores; paged KV) and section "答案不在算法里" (fixed block size; validation on a W8A8-FP8 model).
 //
-// Same work decomposition as the bf16 kernel (bsa_bf16.hip):
+// Same work decomposition and softmax as the bf16 kernel (bsa_bf16.hip), including two query heads of a
+// KV group per 8-wave workgroup when the group size is even (HEADS = 2):
 //  * S^T = K Q^T runs on the fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales, twice the
 //    bf16 rate) on the e4m3 codes: exact products, fp32 accumulation; the logits are scaled by
 //    q_scale[h] * k_scale[g] / sqrt(d) inside the exp2 argument.  K sub-tiles (64 keys x 128 bytes) go
-//    global -> LDS with global_load_lds_dwordx4 into a swizzled tile (slot ^ ((row >> 1) & 7)); each lane
-//    reads its 32-byte operand with two ds_read_b128.
+//    global -> LDS with buffer loads that write LDS (scalar sub-tile base, fixed per-lane offsets; rows past
+//    the request's end read as zeros) into a swizzled tile (slot ^ ((row >> 1) & 7)); each lane reads its
+//    32-byte operand with two ds_read_b128.  Small pages look up one page per row.
 //  * O^T = V^T P^T stays on the bf16 matrix cores with P in bf16: rounding P to e4m3 (3 mantissa bits)
 //    misses the fp8 output tolerance on rows with few keys.  V is converted to bf16 once per sub-tile while
-//    it is staged (global -> registers -> v_cvt_scalef32_pk_bf16_fp8 -> LDS, each thread 1/256 of the tile,
-//    one sub-tile ahead), into the same swizzled bf16 tile the bf16 kernel reads with ds_read_b64_tr_b16.
+//    it is staged (global -> registers -> v_cvt_scalef32_pk_bf16_fp8 -> LDS, each thread 1/(256 HEADS) of
+//    the tile, one sub-tile ahead), into the same swizzled bf16 tile the bf16 kernel reads with
+//    ds_read_b64_tr_b16.
+//  * softmax without a per-tile row max: the reference is set from a row's first visible keys and moves
+//    only when a tile's sum of P exceeds 2^32 (the tile is then recomputed from K, still in LDS); the row
+//    sum adds the rounded P pairs (v_dot2_f32_bf16).
 //  * v_scale[g] multiplies the output at the end.
 #include "stem_internal.h"
 
@@ -25,14 +31,19 @@ namespace {
 constexpr int D = 128;
 constexpr int B = 128;
 constexpr int KT = 64;
-constexpr int NT = 256;
 constexpr int KTILE = KT * D;      // bytes per K sub-tile (fp8)
 constexpr int VTILE = KT * D * 2;  // bytes per V sub-tile (converted to bf16)
 constexpr int kMaxList = 2048;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units (p <= 256 fits bf16)
+// List entries: block index in the low bits, one selection bit per head of the workgroup.
+constexpr uint32_t kBlockBits = 0x3FFF;
+constexpr uint32_t kSelFirst = 0x4000;
+constexpr uint32_t kSelSecond = 0x8000;
+constexpr float kNoReference = -1e29f;
+constexpr float kOverflow = 4294967296.0f;
+// Buffer resource word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts.
+constexpr int kBufDword3 = 0x00020000;
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
-typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -57,8 +68,13 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 }
 
 // PAGE: 0 contiguous K/V, 1 pages of a multiple of 64 tokens (one page per sub-tile), 2 smaller pages.
-template <int PAGE, bool MASKED>
-__global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
+template <int PAGE, bool MASKED, int HEADS>
+__global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs a) {
+  constexpr int NT = 256 * HEADS;
+  constexpr int KPARTS = 2 / HEADS;    // 1 KB K loads per wave per sub-tile
+  constexpr int VCODES = KT * D / NT;  // V codes each thread stages per sub-tile (32 or 16)
+  constexpr int VTPR = D / VCODES;     // threads per V row
+  constexpr int VCH = VCODES / 8;      // 16-byte bf16 chunks each thread stores
   __shared__ __align__(1024) uint8_t kbuf0[KTILE], kbuf1[KTILE], vbuf0[VTILE], vbuf1[VTILE];
   __shared__ uint16_t list[MASKED ? kMaxList : 1];
   __shared__ int list_len;
@@ -68,41 +84,45 @@ __global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int half = lane >> 5;
+  const int hsel = HEADS == 2 ? wave >> 2 : 0;  // head of the workgroup this wave serves
+  const int wq = HEADS == 2 ? wave & 3 : wave;   // 32-row slice of the query block
+  const uint32_t mine = hsel ? kSelSecond : kSelFirst;
 
-  // ---- work item (XCD-aware, KV-head-major, longest rows first)
+  // ---- work item (XCD-aware, KV-head-major, longest rows first); HEADS query heads of one KV group
   const int grp = a.hq / a.hkv;
+  const int hgroups = grp / HEADS;
   int64_t logical = blockIdx.x;
   if (a.xcd_remap) {
     const int64_t per = (int64_t)gridDim.x / 8;
     logical = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
   }
-  const int64_t per_g = a.NB * grp;
+  const int64_t per_g = a.NB * hgroups;
   const int g = (int)(logical / per_g);
   const int64_t rem = logical % per_g;
-  const int64_t ib = a.NB - 1 - rem / grp;
-  const int h = g * grp + (int)(rem % grp);
+  const int64_t ib = a.NB - 1 - rem / hgroups;
+  const int h0 = g * grp + HEADS * (int)(rem % hgroups);
+  const int h = h0 + hsel;
   const int r = find_request(a.rt, (int)ib);
   const int i = (int)ib - a.rt.cu_blocks[r];
   const int tb = a.rt.cu_seqlens[r];
   const int L = a.rt.cu_seqlens[r + 1] - tb;
+  auto mask_row = [&](int t) { return a.mask + ((int64_t)(h0 + t) * a.NB + ib) * a.mask_words; };
 
-  // ---- list of selected blocks
+  // ---- list of selected blocks (union over the workgroup's heads, one selection bit per head)
   int nsel;
   if constexpr (MASKED) {
     if (wave == 0) {
-      const uint32_t* mrow = a.mask + ((int64_t)h * a.NB + ib) * a.mask_words;
       const int nwords = (i >> 5) + 1;
       int base = 0;
       for (int w0 = 0; w0 < nwords; w0 += 64) {
         const int w = w0 + lane;
-        uint32_t word = 0;
+        uint32_t wa = 0, wb = 0;
         if (w < nwords) {
-          word = mrow[w];
-          if (w == nwords - 1) {
-            const int nb = (i & 31) + 1;
-            word &= (nb == 32) ? 0xFFFFFFFFu : ((1u << nb) - 1u);
-          }
+          const uint32_t keep = (w == nwords - 1 && (i & 31) != 31) ? ((1u << ((i & 31) + 1)) - 1u) : 0xFFFFFFFFu;
+          wa = mask_row(0)[w] & keep;
+          if (HEADS == 2) wb = mask_row(1)[w] & keep;
         }
+        uint32_t word = wa | wb;
         const int c = __popc(word);
         int incl = c;
         for (int o = 1; o < 64; o <<= 1) {
@@ -112,7 +132,8 @@ __global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
         int pos = base + incl - c;
         while (word) {
           const int bit = __ffs(word) - 1;
-          list[pos++] = (uint16_t)(w * 32 + bit);
+          const uint32_t sel = (((wa >> bit) & 1u) ? kSelFirst : 0u) | (((wb >> bit) & 1u) ? kSelSecond : 0u);
+          list[pos++] = (uint16_t)((uint32_t)(w * 32 + bit) | sel);
           word &= word - 1;
         }
         base += __shfl(incl, 63, 64);
@@ -127,7 +148,7 @@ __global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
   const int nsub = nsel * 2;
 
   // ---- Q fragments (B operand of S^T): 32 bytes of dims 64kk + 32half.. per k-step
-  const int qr = wave * 32 + l32;
+  const int qr = wq * 32 + l32;
   const int qpos = i * B + qr;
   const bool qvalid = qpos < L;
   i32x8 qf[2];
@@ -146,57 +167,78 @@ __global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
   const float c2 = a.scale_log2 * a.q_scale[h] * a.k_scale[g];
   const float v_scale = a.v_scale[g];
 
-  // ---- K loader: instruction m (0, 1) of this wave fills LDS chunk 2*wave + m = tile rows
-  //      8*(2*wave + m) + lane/8, slot lane & 7 (16 bytes); the lane fetches the swizzled source chunk.
   const int64_t row_stride = (int64_t)a.hkv * D;
   const uint8_t* kbase_all = (const uint8_t*)a.k;
   const uint8_t* vbase_all = (const uint8_t*)a.v;
   const int64_t head_off = (int64_t)g * D;
 
-  auto sub_key0 = [&](int u) -> int {
-    const int j = MASKED ? (int)list[u >> 1] : (u >> 1);
-    return j * B + (u & 1) * KT;
+  auto entry = [&](int u) -> uint32_t {
+    if constexpr (MASKED) return (uint32_t)list[u >> 1];
+    else return (uint32_t)(u >> 1) | kSelFirst | kSelSecond;
   };
+  auto sub_key0 = [&](uint32_t e, int u) -> int { return (int)(e & kBlockBits) * B + (u & 1) * KT; };
   auto key_row_off = [&](int kp) -> int64_t {
     if (PAGE == 0) return ((int64_t)tb + kp) * row_stride + head_off;
     const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp / a.kv.page_size];
     return ((int64_t)page * a.kv.page_size + (kp % a.kv.page_size)) * row_stride + head_off;
   };
-  // byte offset of tile row `row` of sub-tile u (rows past the end repeat the last key: masked anyway)
+  // byte offset of tile row `row` of the sub-tile starting at key kp0 (rows past the end repeat the last
+  // key: they are causally masked)
   auto tile_row_off = [&](int kp0, int row) -> int64_t {
     if (PAGE != 2 && kp0 + KT <= L) return key_row_off(kp0) + (int64_t)row * row_stride;
     return key_row_off(min(kp0 + row, L - 1));
   };
-  auto issue_k = [&](int u, uint8_t* kdst) {
-    const int kp0 = sub_key0(u);
-    lds_u8* kl = (lds_u8*)kdst + wave * 2048;
+
+  // ---- K loader: instruction m of this wave fills LDS chunk c = KPARTS*wave + m = tile rows 8c + lane/8,
+  //      slot lane & 7 (16 bytes); the lane fetches the swizzled source chunk.
+  // (fixed size 2: lambdas that capture arrays of template-dependent size lose their host stubs)
+  int krow_ld[2], koff_ld[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int row = 8 * (2 * wave + m) + (lane >> 3);
-      const int kc = (lane & 7) ^ ((row >> 1) & 7);
-      __builtin_amdgcn_global_load_lds((const void*)(kbase_all + tile_row_off(kp0, row) + kc * 16), kl + m * 1024,
-                                       16, 0, 0);
+  for (int m = 0; m < KPARTS; ++m) {
+    const int row = 8 * (KPARTS * wave + m) + (lane >> 3);
+    krow_ld[m] = row;
+    koff_ld[m] = row * (int)row_stride + ((lane & 7) ^ ((row >> 1) & 7)) * 16;
+  }
+  auto issue_k = [&](int u, uint8_t* kdst) {
+    const int kp0 = sub_key0(entry(u), u);
+    if (kp0 >= L) return;  // a second half-block past the end of the request: nothing to load
+    lds_u8* kl = (lds_u8*)kdst + wave * (KPARTS * 1024);
+    if (PAGE == 0 || PAGE == 1) {
+      const int nrec = min(L - kp0, KT) * (int)row_stride;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kbase_all + key_row_off(kp0)), 0, nrec, kBufDword3);
+#pragma unroll
+      for (int m = 0; m < KPARTS; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, kl + m * 1024, 16, koff_ld[m], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int m = 0; m < KPARTS; ++m) {
+        const int row = krow_ld[m];
+        const int kc = (lane & 7) ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds((const void*)(kbase_all + tile_row_off(kp0, row) + kc * 16),
+                                         kl + m * 1024, 16, 0, 0);
+      }
     }
   };
-  // V: thread t loads 32 codes of tile row t/4 (dims 32(t%4)..), converts them to bf16 and stores four
-  // 16-byte chunks c = 4(t%4) + j at slot c ^ 4(row & 3) of the bf16 tile (256-byte rows); the chunk order
-  // (j + row) & 3 spreads one store instruction of 16 lanes over the 16 bank groups.
-  const int vrow = tid >> 2, vq = tid & 3;
+  // V: thread t loads VCODES codes of tile row t / VTPR (dims VCODES (t % VTPR) ..), converts them to bf16
+  // and stores VCH 16-byte chunks c = VCH (t % VTPR) + j at slot c ^ 4(row & 3) of the bf16 tile (256-byte
+  // rows), in the order (j + row) mod VCH so that one store instruction spreads over the bank groups.
+  const int vrow = tid / VTPR, vq = tid % VTPR;
   uint4 vraw[2];
   auto load_v = [&](int u) {
-    const uint8_t* src = vbase_all + tile_row_off(sub_key0(u), vrow) + 32 * vq;
+    const uint8_t* src = vbase_all + tile_row_off(sub_key0(entry(u), u), vrow) + VCODES * vq;
     vraw[0] = *(const uint4*)src;
-    vraw[1] = *(const uint4*)(src + 16);
+    if (VCODES == 32) vraw[1] = *(const uint4*)(src + 16);
   };
   auto store_v = [&](uint8_t* vdst) {
     const uint32_t w[8] = {vraw[0].x, vraw[0].y, vraw[0].z, vraw[0].w, vraw[1].x, vraw[1].y, vraw[1].z, vraw[1].w};
     lds_u8* row = (lds_u8*)vdst + vrow * 256;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = (jj + vrow) & 3;  // chunk j holds dims 32vq + 8j .. +8 = codes w[2j], w[2j+1]
+    for (int jj = 0; jj < VCH; ++jj) {
+      const int j = (jj + vrow) & (VCH - 1);  // chunk j holds dims VCODES vq + 8j .. +8 = codes w[2j], w[2j+1]
       const i32x4 c = {(int)fp8x2_to_bf16x2<false>(w[2 * j]), (int)fp8x2_to_bf16x2<true>(w[2 * j]),
                        (int)fp8x2_to_bf16x2<false>(w[2 * j + 1]), (int)fp8x2_to_bf16x2<true>(w[2 * j + 1])};
-      const int chunk = 4 * vq + j;
+      const int chunk = VCH * vq + j;
       *(__attribute__((address_space(3))) i32x4*)(row + 16 * (chunk ^ (4 * (vrow & 3)))) = c;
     }
   };
@@ -235,50 +277,54 @@ __global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
       load_v(u + 1);
       issue_k(u + 1, knext);
     }
-    const int kp0 = sub_key0(u);
+    const uint32_t e = entry(u);
+    const int kp0 = sub_key0(e, u);
     const bool diag = (kp0 / B) == i;
-    if (!(diag && kp0 > i * B + wave * 32 + 31)) {  // else every key of this sub-tile is after the wave's rows
+    // nothing to compute: the sub-tile starts past the request's end, or (diagonal block) every key is
+    // after the wave's rows, or the wave's head did not select the block
+    const bool idle = kp0 >= L || (diag && kp0 > i * B + wq * 32 + 31) || !(e & mine);
+    if (!idle) {
       const lds_u8* Kt = (const lds_u8*)kcur;
       const lds_u8* Vt = (const lds_u8*)vcur;
       f32x16 s0, s1;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        s0[x] = 0.f;
-        s1[x] = 0.f;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int sa = 4 * kk + 2 * half;
-        const uint32_t o0 = krow + 16 * (sa ^ kx), o1 = krow + 16 * ((sa + 1) ^ kx);
-        const i32x4 a00 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o0);
-        const i32x4 a01 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o1);
-        const i32x4 a10 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o0 + 32 * 128);
-        const i32x4 a11 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o1 + 32 * 128);
-        const i32x8 f0 = {a00[0], a00[1], a00[2], a00[3], a01[0], a01[1], a01[2], a01[3]};
-        const i32x8 f1 = {a10[0], a10[1], a10[2], a10[3], a11[0], a11[1], a11[2], a11[3]};
-        s0 = mfma_fp8(f0, qf[kk], s0);
-        s1 = mfma_fp8(f1, qf[kk], s1);
-      }
-      if (diag) {
+      auto scores = [&]() {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int kl = 8 * (x >> 2) + 4 * half + (x & 3);
-          if (kp0 + kl > qpos) s0[x] = -INFINITY;
-          if (kp0 + 32 + kl > qpos) s1[x] = -INFINITY;
+          s0[x] = 0.f;
+          s1[x] = 0.f;
         }
-      }
-      float mx = max3(s0[0], s0[1], s1[0]);
-      mx = max3(mx, s0[2], s1[1]);
 #pragma unroll
-      for (int x = 3; x < 16; ++x) mx = max3(mx, s0[x], s1[x - 1]);
-      mx = fmaxf(mx, s1[15]);
-      {
+        for (int kk = 0; kk < 2; ++kk) {
+          const int sa = 4 * kk + 2 * half;
+          const uint32_t o0 = krow + 16 * (sa ^ kx), o1 = krow + 16 * ((sa + 1) ^ kx);
+          const i32x4 a00 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o0);
+          const i32x4 a01 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o1);
+          const i32x4 a10 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o0 + 32 * 128);
+          const i32x4 a11 = *(const __attribute__((address_space(3))) i32x4*)(Kt + o1 + 32 * 128);
+          const i32x8 f0 = {a00[0], a00[1], a00[2], a00[3], a01[0], a01[1], a01[2], a01[3]};
+          const i32x8 f1 = {a10[0], a10[1], a10[2], a10[3], a11[0], a11[1], a11[2], a11[3]};
+          s0 = mfma_fp8(f0, qf[kk], s0);
+          s1 = mfma_fp8(f1, qf[kk], s1);
+        }
+        if (diag) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int kl = 8 * (x >> 2) + 4 * half + (x & 3);
+            if (kp0 + kl > qpos) s0[x] = -INFINITY;
+            if (kp0 + 32 + kl > qpos) s1[x] = -INFINITY;
+          }
+        }
+      };
+      // Move the reference max to this tile's max (O^T and the sum rescale by 2^(old - new), exact).
+      auto rebase = [&]() {
+        float mx = max3(s0[0], s0[1], s1[0]);
+        mx = max3(mx, s0[2], s1[1]);
+#pragma unroll
+        for (int x = 3; x < 16; ++x) mx = max3(mx, s0[x], s1[x - 1]);
+        mx = fmaxf(mx, s1[15]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      const float mt = mx * c2;
-      if (__ballot(mt > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, mt);
+        const float m_new = fmaxf(m_run, mx * c2);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_part *= alpha;
 #pragma unroll
@@ -286,23 +332,46 @@ __global__ __launch_bounds__(NT, 2) void bsa_fp8_kernel(BsaArgs a) {
 #pragma unroll
           for (int x = 0; x < 16; ++x) o[dt][x] *= alpha;
         m_run = m_new;
-      }
-      const float negm = -m_run;
-      float ps = 0.f;
+      };
+      uint4 pw[4];  // P rounded to bf16 pairs, the B operand of each PV k-step
+      auto exp_pack = [&]() -> float {
+        const float negm = -m_run;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
-        s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
-        ps += s0[x] + s1[x];
+        for (int x = 0; x < 16; ++x) {
+          s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
+          s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
+        }
+        const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const f32x16& st = (mm < 2) ? s0 : s1;
+          const int x0 = 8 * (mm & 1);
+          pw[mm] = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
+                              cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
+          ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].x), ones, ps0, false);
+          ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].y), ones, ps1, false);
+          ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].z), ones, ps0, false);
+          ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[mm].w), ones, ps1, false);
+        }
+        return ps0 + ps1;
+      };
+      // Rebase at the first visible keys of a row; if a tile overflows the reference, compute it again
+      // with a rebase (at most once: after a rebase every P is <= 1).
+      bool force = __ballot(m_run < kNoReference) != 0;
+      float ps;
+      for (;;) {
+        asm volatile("" ::: "memory");  // keep the K reads inside the (rarely repeated) loop body
+        scores();
+        if (force) rebase();
+        ps = exp_pack();
+        if (force || __ballot(!(ps <= kOverflow)) == 0) break;
+        force = true;
       }
       l_part += ps;
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
-        const f32x16& st = (mm < 2) ? s0 : s1;
-        const int x0 = 8 * (mm & 1);
-        const uint4 pw = make_uint4(cvt_bf16x2(st[x0], st[x0 + 1]), cvt_bf16x2(st[x0 + 2], st[x0 + 3]),
-                                    cvt_bf16x2(st[x0 + 4], st[x0 + 5]), cvt_bf16x2(st[x0 + 6], st[x0 + 7]));
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw[mm]);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const lds_u8* vp = Vt + voffs[dt] + mm * 4096;
@@ -353,20 +422,24 @@ bool bsa_fp8_supported(int dtype, int head_dim, int block) {
   return dtype == STEM_FP8_E4M3 && head_dim == D && block == B;
 }
 
-hipError_t launch_bsa_fp8(const BsaArgs& a, bool masked, hipStream_t s) {
-  dim3 grid((unsigned)(a.hq * a.NB));
-  dim3 block(NT);
+template <bool MASKED, int HEADS>
+static hipError_t launch_fp8_heads(const BsaArgs& args, hipStream_t s) {
+  BsaArgs a = args;
+  const int64_t wgs = (int64_t)(a.hq / HEADS) * a.NB;
+  a.xcd_remap = wgs % 8 == 0 ? 1 : 0;
+  const dim3 grid((unsigned)wgs), block(256 * HEADS);
   const int page_mode = !a.kv.paged ? 0 : (a.kv.page_size % KT == 0 ? 1 : 2);
-#define STEM_LAUNCH(PM)                                                                    \
-  do {                                                                                     \
-    if (masked) hipLaunchKernelGGL((bsa_fp8_kernel<PM, true>), grid, block, 0, s, a);      \
-    else hipLaunchKernelGGL((bsa_fp8_kernel<PM, false>), grid, block, 0, s, a);            \
-  } while (0)
-  if (page_mode == 0) STEM_LAUNCH(0);
-  else if (page_mode == 1) STEM_LAUNCH(1);
-  else STEM_LAUNCH(2);
-#undef STEM_LAUNCH
+  if (page_mode == 0) hipLaunchKernelGGL((bsa_fp8_kernel<0, MASKED, HEADS>), grid, block, 0, s, a);
+  else if (page_mode == 1) hipLaunchKernelGGL((bsa_fp8_kernel<1, MASKED, HEADS>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((bsa_fp8_kernel<2, MASKED, HEADS>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+// Two heads per workgroup whenever a KV group has an even number of query heads.
+hipError_t launch_bsa_fp8(const BsaArgs& a, bool masked, hipStream_t s) {
+  const bool pair = (a.hq / a.hkv) % 2 == 0;
+  if (masked) return pair ? launch_fp8_heads<true, 2>(a, s) : launch_fp8_heads<true, 1>(a, s);
+  return pair ? launch_fp8_heads<false, 2>(a, s) : launch_fp8_heads<false, 1>(a, s);
 }
 
 }  // namespace stem
