@@ -329,11 +329,16 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
         __builtin_amdgcn_sched_barrier(0);
       }
       if (diag) {
+        // key kp0 + 8(x/4) + 4 half + x%4 (+32 for s1) is after the query when its constant part
+        // 8(x/4) + x%4 exceeds lim; lim passes through an empty asm so that the compares stay in this
+        // branch (hoisted out of the retry loop they would run on every sub-tile)
+        int lim = qpos - kp0 - 4 * half;
+        asm volatile("" : "+v"(lim));
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int kl = 8 * (x >> 2) + 4 * half + (x & 3);
-          if (kp0 + kl > qpos) s0[x] = -INFINITY;
-          if (kp0 + 32 + kl > qpos) s1[x] = -INFINITY;
+          const int c = 8 * (x >> 2) + (x & 3);
+          if (c > lim) s0[x] = -INFINITY;
+          if (c + 32 > lim) s1[x] = -INFINITY;
         }
       }
     };
