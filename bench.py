@@ -269,11 +269,13 @@ def measure_quantize(dev, torch, reps):
             "note": "a separate quantiser would read bf16 twice and write fp8, then stem_score reads the fp8 again"}
 
 
-def measure_cold(L, q, k, v, p, torch, dev, steps=7):
+def measure_cold(L, q, k, v, p, torch, dev, steps=20, warmup=5):
     """Layer time with the caches evicted before every step (a 1 GiB buffer is overwritten between
-    steps, outside the timed events): median, p10 and p90 over the steps."""
+    steps, outside the timed events): median, p10 and p90 over the steps, after `warmup` untimed ones."""
     rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        L.forward(q, k, v, p.beta, rho, mu)
     times = []
     for _ in range(steps):
         scratch.fill_(1)
@@ -286,7 +288,20 @@ def measure_cold(L, q, k, v, p, torch, dev, steps=7):
     del scratch
     t = np.array(times)
     return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
-            "p90": round(float(np.percentile(t, 90)), 4), "steps": steps}
+            "p90": round(float(np.percentile(t, 90)), 4), "steps": steps, "warmup": warmup}
+
+
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and logical CPU count."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
 
 
 def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
@@ -489,7 +504,7 @@ def main():
         log("[bench] CPU oracle on a bounded sample")
         v_cpu, threads, desc = cpu_baseline(p, x, words, None)
         out["cpu_baseline"] = {"value": round(v_cpu, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                               "sample": desc}
+                               "sample": desc, "host": host_cpu()}
     print(json.dumps(out), flush=True)
 
 
