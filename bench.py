@@ -11,7 +11,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -304,10 +303,12 @@ def host_cpu():
     return {"model": model, "logical_cpus": os.cpu_count()}
 
 
-def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
-    """The oracle, as it stands, on a bounded sample of rows of the same workload: for each sampled
-    (query head, query block) row it pools, scores, takes the TPD budget, selects and attends.
-    Returns (TFLOP/s, threads, description)."""
+def cpu_baseline(p, x, tokens=32768):
+    """The oracle's whole pipeline, as it stands, on a bounded sample of the same workload: the first
+    `tokens` tokens of request 0 (a request of its own, causal from its first token), KV group 0 and its
+    query heads.  Each stage is timed by wall clock: decode (bf16/fp8 bytes to float64) and pooling, block
+    scores, TPD budgets and selection, block-sparse attention.  Returns (TFLOP/s, threads, description,
+    per-stage seconds); the flop count is 4·d per visible selected pair of the sample's own mask."""
     import oracle
     from tests import stem_cases as sc
 
@@ -317,40 +318,43 @@ def cpu_baseline(p, x, words, budget_rows, seconds=12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    r = 0
-    a, b = sc.request_slices(p)[r]
-    n = p.nblocks(r)
+    a, b = sc.request_slices(p)[0]
+    T = min(tokens, b - a)
     grp = p.hq // p.hkv
-    rng = np.random.default_rng(0)
-    g = 0  # one KV group keeps the decode bounded
-    t_start = time.perf_counter()
-    kf = sc.decode_kv(p, x, r, "k", [g])
-    vf = sc.decode_kv(p, x, r, "v", [g])
-    kbar = oracle.pool_blocks(kf, p.block)[0]
-    M = oracle.value_log_magnitude(vf, p.block)[0]
+    heads = list(range(grp))  # the query heads of KV group 0
+    st = {}
+    t = time.perf_counter()
+    q = sc.decode_q(p, x, a, a + T, heads)
+    k = sc.decode_kv(p, x, 0, "k", [0])[:T]
+    v = sc.decode_kv(p, x, 0, "v", [0])[:T]
+    qbar = oracle.pool_blocks(q, p.block)
+    kbar = oracle.pool_blocks(k, p.block)
+    M = oracle.value_log_magnitude(v, p.block)
+    st["decode_pool"] = time.perf_counter() - t
+    t = time.perf_counter()
+    S = oracle.oam_block_scores(qbar, kbar, M, p.beta)
+    st["score"] = time.perf_counter() - t
+    t = time.perf_counter()
+    n = qbar.shape[1]
     budgets = oracle.tpd_budgets(n, p.rho_num, p.rho_den, p.mu_num, p.mu_den)
-    flops = 0
-    rows = 0
-    scale = 1.0 / math.sqrt(p.d)
-    while time.perf_counter() - t_start < seconds:
-        h = g * grp + int(rng.integers(grp))
-        i = int(rng.integers(n))
-        t0, t1 = i * p.block, min((i + 1) * p.block, b - a)
-        qf = sc.decode_q(p, x, a + t0, a + t1, [h])[:, 0]
-        qbar = qf.mean(axis=0)
-        S = qbar @ kbar[: i + 1].T / math.sqrt(p.d) + p.beta * M[: i + 1]
-        sel = oracle.select_row(S, int(budgets[i]))
-        key_idx = np.concatenate([np.arange(j * p.block, min((j + 1) * p.block, b - a)) for j in sel])
-        oracle.attention_rows(qf, np.arange(t0, t1), kf[:, 0], vf[:, 0], key_idx, scale)
-        sizes = np.array([min(p.block, (b - a) - j * p.block) for j in sel])
-        qs = t1 - t0
-        vis = sum(qs * s for j, s in zip(sel, sizes) if j < i) + (qs * (qs + 1) // 2 if i in sel else 0)
-        flops += 4 * p.d * vis
-        rows += 1
-    dt = time.perf_counter() - t_start
-    desc = (f"{rows} random (head, block) rows of KV group {g}, each pooled, scored, budgeted, selected and "
-            f"attended by the fp64 oracle ({dt:.1f} s incl. decoding/pooling that group's K and V)")
-    return flops / dt / 1e12, threads, desc
+    mask = oracle.select_all(S, budgets)
+    st["budget_select"] = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.block_sparse_attention(q, k, v, mask, p.block)
+    st["attention"] = time.perf_counter() - t
+    # visible selected pairs: full blocks below the diagonal, the causal triangle on it (ragged last block)
+    sizes = np.array([min(p.block, T - j * p.block) for j in range(n)], dtype=np.int64)
+    vis = 0
+    for h in range(len(heads)):
+        for i in range(n):
+            sel = np.nonzero(mask[h, i, : i + 1])[0]
+            vis += int(sizes[i] * sizes[sel[sel < i]].sum())
+            if mask[h, i, i]:
+                vis += int(sizes[i] * (sizes[i] + 1) // 2)
+    dt = sum(st.values())
+    desc = (f"the oracle's pipeline on the first {T} tokens of request 0, KV group 0 and its {len(heads)} query "
+            f"heads ({n} blocks, {dt:.1f} s)")
+    return 4 * p.d * vis / dt / 1e12, threads, desc, {k_: round(v_, 3) for k_, v_ in st.items()}
 
 
 def traffic_from_profile(src_sha):
@@ -502,9 +506,9 @@ def main():
         out["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle on a bounded sample")
-        v_cpu, threads, desc = cpu_baseline(p, x, words, None)
+        v_cpu, threads, desc, stages = cpu_baseline(p, x)
         out["cpu_baseline"] = {"value": round(v_cpu, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                               "sample": desc, "host": host_cpu()}
+                               "sample": desc, "stages_s": stages, "host": host_cpu()}
     print(json.dumps(out), flush=True)
 
 
