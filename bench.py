@@ -303,7 +303,7 @@ def host_cpu():
     return {"model": model, "logical_cpus": os.cpu_count()}
 
 
-def cpu_baseline(p, x, tokens=32768):
+def cpu_baseline(p, x, tokens=65536):
     """The oracle's whole pipeline, as it stands, on a bounded sample of the same workload: the first
     `tokens` tokens of request 0 (a request of its own, causal from its first token), KV group 0 and its
     query heads.  Each stage is timed by wall clock: decode (bf16/fp8 bytes to float64) and pooling, block
