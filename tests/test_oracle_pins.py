@@ -179,6 +179,23 @@ def test_tpd_budget_invariants(n, rho, mu):
         assert rs[-1] == mu_f * x
 
 
+@pytest.mark.parametrize("n,rho,T,k_start,dense_rows", [
+    (32, 25, 132, 5.247, 5), (256, 25, 8224, 41.477, 40), (512, 25, 32832, 82.881, 79),
+    (1024, 10, 52480, 62.460, 61), (1024, 25, 131200, 165.688, 158), (1024, 50, 262400, 373.538, 337)])
+def test_tpd_against_an_independent_exact_computation(n, rho, T, k_start, dense_rows):
+    """Totals, line start k_start* (to 3 decimals) and the number of leading rows whose integer budget is
+    their whole causal row (k_i = i + 1), from a separate exact computation made when the workloads were
+    planned (mu = 7/10); at n = 1024 and 25% the line also ends at k_end* = 115.982."""
+    assert oracle.tpd_total(n, rho, 100) == T
+    x, rs = oracle.tpd_solve(n, T, Fraction(7, 10))
+    assert abs(float(x) - k_start) < 5e-4
+    k = oracle.tpd_budgets(n, rho, 100, 7, 10)
+    full = k == np.arange(1, n + 1)
+    assert int(full.sum()) == dense_rows and bool(full[:dense_rows].all())
+    if (n, rho) == (1024, 25):
+        assert abs(float(rs[-1]) - 115.982) < 5e-4
+
+
 def test_tpd_full_budget_is_dense_and_min_budget_is_one_per_row():
     for n in (1, 2, 5, 40):
         assert np.array_equal(oracle.tpd_budgets(n, 1, 1, 7, 10), np.arange(1, n + 1))
