@@ -165,20 +165,33 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
     }
   }
   if (kind == 2) {
-    // All lanes of a head must take part in the shuffle: iterate a uniform trip count per row slot.
-    for (int t = t0 + rs; t < t0 + a.B; t += tr) {
-      float ss = 0.f;
-      if (active && t < t1) {
+    // All lanes of a head must take part in the shuffles: a uniform trip count per row slot; four rows per
+    // trip so that four loads are in flight (the rows' log-norms are added in row order).
+    for (int t = t0 + rs; t < t0 + a.B; t += 4 * tr) {
+      uint4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tj = t + j * tr;
+        w[j] = (active && tj < t1) ? load(tj) : make_uint4(0u, 0u, 0u, 0u);
+      }
+      float ss[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
         float x[EPL];
-        decode16<EB>(load(t), x);
+        decode16<EB>(w[j], x);
+        ss[j] = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           const float y = x[e] * vscale;
-          ss = fmaf(y, y, ss);
+          ss[j] = fmaf(y, y, ss[j]);
         }
       }
-      for (int m = 1; m < hl; m <<= 1) ss += __shfl_xor(ss, m, 64);
-      if (active && t < t1) lacc += 0.5f * logf(ss);
+      for (int m = 1; m < hl; m <<= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss[j] += __shfl_xor(ss[j], m, 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (active && t + j * tr < t1) lacc += 0.5f * logf(ss[j]);
     }
   }
 
