@@ -68,15 +68,15 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a) {
   constexpr int EPL = 16 / EB;  // elements per lane
   const int ib = blockIdx.x;
   int job = blockIdx.y;
-  int kind;  // 0 = Q mean, 1 = K mean, 2 = V log-norm mean
-  if (job < a.q_chunks) {
-    kind = 0;
-  } else if (job < a.q_chunks + a.kv_chunks) {
-    kind = 1;
-    job -= a.q_chunks;
-  } else {
+  int kind;  // 0 = Q mean, 1 = K mean, 2 = V log-norm mean (V jobs first: they take longest per byte)
+  if (job < a.kv_chunks) {
     kind = 2;
-    job -= a.q_chunks + a.kv_chunks;
+  } else if (job < 2 * a.kv_chunks) {
+    kind = 1;
+    job -= a.kv_chunks;
+  } else {
+    kind = 0;
+    job -= 2 * a.kv_chunks;
   }
   const int H = kind == 0 ? a.hq : a.hkv;
   const int d = a.d;
