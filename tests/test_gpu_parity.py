@@ -120,6 +120,9 @@ SMALL = [
     # an odd number of query heads per KV head: one head per workgroup, with pages of 64 and of 16 tokens
     ("paged_ragged_bf16", dict(lens=(300, 700), hq=3, hkv=1)),
     ("paged_ragged_bf16", dict(lens=(257, 1000), hq=3, hkv=3, page_size=16)),
+    # fp8 with two query heads per workgroup over pages of 64 and of 32 tokens
+    ("paged_ragged_bf16", dict(lens=(300, 700), hq=4, hkv=2, dtype="fp8")),
+    ("paged_ragged_bf16", dict(lens=(129, 500), hq=8, hkv=2, page_size=32, dtype="fp8")),
 ]
 
 
@@ -142,8 +145,8 @@ def test_small_case_all_outputs(dev, name, over):
     assert lerr <= 10 * tmax
 
 
-@pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[9], SMALL[11]],
-                         ids=["f32", "bf16", "fp8", "paged"])
+@pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[3], SMALL[9], SMALL[11]],
+                         ids=["f32", "bf16", "bf16-one-head-per-workgroup", "fp8", "paged"])
 def test_dense_mode_matches_textbook_attention(dev, name, over):
     """mask = NULL runs dense causal attention: the 100%-budget special case of the oracle."""
     p = synth.make_problem(name, **over)
