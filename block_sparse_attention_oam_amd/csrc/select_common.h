@@ -53,15 +53,36 @@ template <int NS>
 __device__ __forceinline__ void select_row(const uint32_t (&key)[NS], int nslot, int k, int lane,
                                            uint32_t* mrow, int mask_words) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // k-th largest key: the largest tau with #{key >= tau} >= k (valid keys are >= 0x007FFFFF > 0)
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  // k-th largest key: the largest tau with #{key >= tau} >= k (valid keys are >= 0x007FFFFF > 0, invalid
+  // ones 0).  All valid keys share the bits above the highest bit where the row's largest and smallest
+  // valid keys differ, so tau does too: the bit-by-bit search starts below that common prefix.  It stops
+  // as soon as exactly k keys reach the candidate (those are then the k largest, with no tie at the
+  // boundary), which gives the same selection as running it to the last bit.
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (s < nslot && key[s] != 0u) {
+      kmax = max(kmax, key[s]);
+      kmin = min(kmin, key[s]);
+    }
+  for (int o = 1; o < 64; o <<= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+  }
+  const uint32_t diff = kmax ^ kmin;
+  const int top = diff == 0u ? -1 : 31 - __clz(diff);  // highest differing bit (-1: all keys equal)
+  uint32_t tau;                                          // the common prefix, lower bits clear
+  if (top < 0) tau = kmax;
+  else if (top == 31) tau = 0u;
+  else tau = kmax & ~((2u << top) - 1u);
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       if (s < nslot) cnt += __popcll(__ballot(key[s] >= cand));
     if (cnt >= k) tau = cand;
+    if (cnt == k) break;
   }
   int gt = 0;
 #pragma unroll
