@@ -44,6 +44,50 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) <= exported
 
 
+def _declared_prototypes():
+    """{name: (return type text, [parameter type texts])} from the header (comments stripped)."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?[a-z_0-9]+\s*\*?)\s*([a-z_0-9]+)\s*\(([^)]*)\)\s*;", src, flags=re.M):
+        ret, name, params = m.group(1), m.group(2), m.group(3).strip()
+        args = [] if params in ("", "void") else [a.strip() for a in params.split(",")]
+        protos[name] = (re.sub(r"\s+", " ", ret).strip(), args)
+    return protos
+
+
+def _ctype_of(text):
+    """The ctypes type a C parameter or return type must map to (pointers of any kind: void pointer or a
+    ctypes pointer / structure pointer)."""
+    t = re.sub(r"\b(const|struct)\b", "", text)
+    if "*" in t:
+        return "pointer"
+    base = t.split()[0] if t.split() else t
+    return {"int": ctypes.c_int, "int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "size_t": ctypes.c_size_t,
+            "float": ctypes.c_float, "double": ctypes.c_double}[base]
+
+
+def test_binding_signatures_match_the_header():
+    """Every declared function: the binding's argument count and the scalar argument and return types agree
+    with the prototype (pointer parameters are pointers on both sides)."""
+    protos = _declared_prototypes()
+    assert set(protos) == set(stem.EXPORTS)
+    L = stem.lib()
+    for name, (ret, args) in protos.items():
+        f = getattr(L, name)
+        assert len(f.argtypes) == len(args), (name, len(f.argtypes), args)
+        for want_text, got in zip(args, f.argtypes):
+            want = _ctype_of(want_text.rsplit(" ", 1)[0] if " " in want_text and "*" not in want_text.rsplit(" ", 1)[1] else want_text)
+            if want == "pointer":
+                assert got is ctypes.c_void_p or issubclass(got, ctypes._Pointer) or got is ctypes.c_char_p, (name, want_text, got)
+            else:
+                assert ctypes.sizeof(got) == ctypes.sizeof(want) and got._type_ == want._type_, (name, want_text, got)
+        want_ret = _ctype_of(ret)
+        if want_ret == "pointer":
+            assert f.restype in (ctypes.c_char_p, ctypes.c_void_p), (name, ret, f.restype)
+        else:
+            assert f.restype is not None and ctypes.sizeof(f.restype) == ctypes.sizeof(want_ret), (name, ret, f.restype)
+
+
 def test_status_strings():
     L = stem.lib()
     for s, name in [(0, "STEM_OK"), (-1, "STEM_E_INVALID_ARG"), (-2, "STEM_E_UNSUPPORTED"),
