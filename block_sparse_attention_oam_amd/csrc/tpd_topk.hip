@@ -5,7 +5,9 @@
 // 快几十倍" (budget generation is one formula per position and is fused with the selection sort, so no
 // budget tensor goes through HBM).
 //
-// One wavefront handles kRowsPerWave consecutive query-block rows (h, i) of one request:
+// One wavefront handles about kRowsPerWave query-block rows (h, i) of one request, i = i0, i0 + stride, ...
+// (strided, so that every wave gets a similar mix of short and long rows; the next row's scores are
+// loaded while the current row is selected):
 //   1. the request's budget plan (capped prefix / linear middle / floored suffix, tpd_budget.h) is solved
 //      by a 64-way parallel search: each lane evaluates one breakpoint predicate, a ballot picks the
 //      sub-interval, about log_64(n) rounds;
@@ -32,22 +34,35 @@ __global__ __launch_bounds__(kWaves * 64) void topk_kernel(TopkArgs a) {
   const int n = a.rt.cu_blocks[r + 1] - (int)cb;
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
-  const int i_begin = (blockIdx.x * kWaves + wave) * kRowsPerWave;
+  // rows i_begin, i_begin + stride, ... (a mix of short and long rows per wave)
+  const int i_begin = blockIdx.x * kWaves + wave;
+  const int stride = gridDim.x * kWaves;
   if (i_begin >= n) return;
   const TpdPlan plan = wave_plan(n, a.rho_num, a.rho_den, a.mu_num, a.mu_den, lane);
-  const int i_end = min(i_begin + kRowsPerWave, n);
 
-  for (int i = i_begin; i < i_end; ++i) {
+  // raw scores of the next row are loaded while the current row is selected
+  float nxt[NS];
+  auto load_row = [&](int i, float* v) {
+    const float* srow = a.scores + ((int64_t)h * a.NB + cb + i) * a.stride;
+    const int nslot = i / 64 + 1;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int j = lane + 64 * s;
+      v[s] = (s < nslot && j <= i) ? srow[j] : 0.f;
+    }
+  };
+  load_row(i_begin, nxt);
+  for (int i = i_begin; i < n; i += stride) {
     const int64_t row = (int64_t)h * a.NB + cb + i;
-    const int k = (int)tpd_row_budget(plan, i);
-    const float* srow = a.scores + row * a.stride;
     const int nslot = i / 64 + 1;
     uint32_t key[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int j = lane + 64 * s;
-      key[s] = (s < nslot && j <= i) ? ord_key(srow[j]) : 0u;
+      key[s] = (s < nslot && j <= i) ? ord_key(nxt[s]) : 0u;
     }
+    if (i + stride < n) load_row(i + stride, nxt);
+    const int k = (int)tpd_row_budget(plan, i);
     select_row<NS>(key, nslot, k, lane, a.mask + row * a.mask_words, a.mask_words);
     if (lane == 0) a.counts[row] = k;
   }
