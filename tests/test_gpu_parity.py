@@ -145,6 +145,53 @@ def test_small_case_all_outputs(dev, name, over):
     assert lerr <= 10 * tmax
 
 
+def _random_problem(seed):
+    """A seeded random small problem over the supported space: dtype, head_dim and block cycle with the
+    seed (so that the twelve cases cover each kernel), the rest is drawn: GQA ratio, 1-3 requests (some
+    empty, some shorter than a block), contiguous or paged K/V (pages of 16-96 tokens, also ones that do
+    not divide the block), budget, mu and beta."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "fp8", "bf16", "f32"][seed % 4]
+    block = [128, 128, 64][seed % 3]
+    d = 64 if seed % 5 == 2 else 128
+    hq, hkv = [(2, 1), (3, 1), (4, 1), (4, 2), (6, 2), (8, 2), (2, 2), (6, 3)][rng.integers(8)]
+    nreq = int(rng.integers(1, 4))
+    lens = []
+    for _ in range(nreq):
+        u = rng.random()
+        lens.append(0 if u < 0.1 else int(rng.integers(1, 200)) if u < 0.4 else int(rng.integers(200, 1500)))
+    if sum(lens) == 0:
+        lens[0] = 333
+    mu = [(7, 10), (1, 1), (1, 2)][rng.integers(3)]
+    over = dict(lens=tuple(lens), hq=hq, hkv=hkv, d=d, block=block, dtype=dtype,
+                rho_num=int(rng.choice([10, 25, 50, 100])), beta=float(rng.choice([0.2, 0.0, 0.5])),
+                mu_num=mu[0], mu_den=mu[1])
+    if seed % 5 in (1, 3):
+        over.update(paged=True, page_size=int(rng.choice([16, 32, 48, 64, 96])))
+    return synth.make_problem("llama_32k_bf16", **over)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_problem_all_outputs(dev, seed):
+    """Every output of the three stages against the oracle on a seeded random problem."""
+    p = _random_problem(seed)
+    _log(f"[random {seed}] lens {p.lens} hq {p.hq} hkv {p.hkv} d {p.d} block {p.block} {p.dtype} "
+         f"paged {p.paged}/{p.page_size} rho {p.rho_num}% mu {p.mu_num}/{p.mu_den} beta {p.beta}")
+    x = synth.make_inputs(p, seed=seed)
+    ref1 = sc.oracle_stage1(p, x)
+    budgets = sc.oracle_budgets(p)
+    masks = sc.oracle_masks([s for *_, s in ref1], budgets)
+    g = _run(p, x, dev, masks_for_bsa=masks)
+    _check_stage1(p, g, ref1)
+    ties = sc.check_selection(p, [s for *_, s in ref1], budgets, g["words"], g["counts"])
+    ora = sc.oracle_attention(p, x, masks)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
+    tmax, tmean = sc.TOL[p.dtype]
+    _log(f"  near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
+    assert mx <= tmax and mean <= tmean
+    assert lerr <= 10 * tmax
+
+
 @pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[3], SMALL[9], SMALL[11]],
                          ids=["f32", "bf16", "bf16-one-head-per-workgroup", "fp8", "paged"])
 def test_dense_mode_matches_textbook_attention(dev, name, over):
