@@ -33,6 +33,22 @@ def test_header_compiles_as_c99():
     assert r.returncode == 0, r.stderr
 
 
+def test_plain_c_program_uses_the_abi(tmp_path):
+    """A C99 program (tests/c_abi_consumer.c) compiled with gcc against the header, linked against the
+    library: host-only entry points and host-side validation, called from C."""
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.skip("libstem.so is not built")
+    exe = str(tmp_path / "c_abi_consumer")
+    libdir = os.path.dirname(_abi.LIB_PATH)
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_consumer.c")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), src, "-L", libdir,
+                        "-lstem", "-Wl,-rpath," + libdir, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "c consumer ok" in r.stdout
+
+
 def test_library_exports_every_declared_symbol():
     declared = _declared_functions()
     assert set(declared) == set(stem.EXPORTS)
