@@ -192,6 +192,46 @@ def test_random_small_problem_all_outputs(dev, seed):
     assert lerr <= 10 * tmax
 
 
+def test_plain_c_program_runs_the_path(dev, tmp_path):
+    """A C99 program (tests/c_abi_pipeline.c) built with gcc against stem.h and the HIP runtime's C API
+    runs stem_score, stem_tpd_topk and bsa_prefill on seeded inputs; its selection and outputs are
+    checked against the oracle like the Python binding's."""
+    import os
+    import subprocess
+    from block_sparse_attention_oam_amd import _abi
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    libdir = os.path.dirname(_abi.LIB_PATH)
+    exe = str(tmp_path / "c_abi_pipeline")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        "-I" + os.path.join(root, "include"), os.path.join(here, "c_abi_pipeline.c"), "-L" + libdir,
+                        "-lstem", "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath," + libdir, "-Wl,-rpath,/opt/rocm/lib",
+                        "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    p = synth.make_problem("llama_32k_bf16", lens=(1100,), hq=4, hkv=2)
+    x = synth.make_inputs(p, seed=11)
+    for name in ("q", "k", "v"):
+        np.ascontiguousarray(x[name]).tofile(str(tmp_path / (name + ".bin")))
+    _log("[c pipeline] 1100 tokens, 4 query / 2 KV heads")
+    r = subprocess.run([exe, str(tmp_path), "1100", "4", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    n = p.nblocks(0)
+    words = np.fromfile(str(tmp_path / "mask.bin"), dtype=np.uint32).reshape(p.hq, n, (n + 31) // 32)
+    counts = np.fromfile(str(tmp_path / "counts.bin"), dtype=np.int32).reshape(p.hq, n)
+    bits = np.fromfile(str(tmp_path / "out.bin"), dtype=np.uint16).reshape(1100, p.hq, p.d)
+    out = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    lse = np.fromfile(str(tmp_path / "lse.bin"), dtype=np.float32).reshape(p.hq, 1100).astype(np.float64)
+    ref1 = sc.oracle_stage1(p, x)
+    budgets = sc.oracle_budgets(p)
+    sc.check_selection(p, [s for *_, s in ref1], budgets, words, counts)
+    gmask = sc.unpack_mask(words, n) & np.tril(np.ones((n, n), dtype=bool))[None]
+    ora = sc.oracle_attention(p, x, [gmask])
+    mx, mean, lerr = sc.compare_attention(p, ora, out, lse)
+    _log(f"  out max {mx:.2e} mean {mean:.2e} lse {lerr:.2e}")
+    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= 0.2
+
+
 @pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[3], SMALL[9], SMALL[11]],
                          ids=["f32", "bf16", "bf16-one-head-per-workgroup", "fp8", "paged"])
 def test_dense_mode_matches_textbook_attention(dev, name, over):
