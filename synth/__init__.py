@@ -25,7 +25,7 @@ innovations (all groups, packed tokens), page permutation.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import numpy as np
 from scipy.signal import lfilter

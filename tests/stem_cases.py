@@ -3,8 +3,6 @@ comparisons to the GPU results.  Imports the oracle (test infrastructure) and th
 side goes only through the library's C ABI."""
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 import oracle
