@@ -413,15 +413,16 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
   };
 
   // One sub-tile: wait for its loads, start the next sub-tile's loads into the other buffer (free since
-  // the barrier), compute.  With two heads and a list, the second head's waves issue their share of the
-  // next loads right after the barrier and the first head's waves theirs at the end of the step: the
-  // second head's waves, which each SIMD's matrix pipe serves last, then no longer queue behind the first
-  // head's loads in the memory pipe (1.1% faster at 128K with 25% of the blocks, 1.3% at 32K; dense
-  // causal, slower that way, issues all loads after the barrier).
+  // the barrier), compute.  With two heads and a list of at most 3/4 of the row's causal blocks, the
+  // second head's waves issue their share of the next loads right after the barrier and the first head's
+  // waves theirs at the end of the step: the second head's waves, which each SIMD's matrix pipe serves
+  // last, then no longer queue behind the first head's loads in the memory pipe (about 2% faster at 25%
+  // and 50% of the blocks; fuller rows, dense causal and the in-loop variant were slower that way and
+  // issue all loads after the barrier).
+  const bool at_end = HEADS == 2 && MASKED && !INLOOP && hsel == 0 && 4 * nsel <= 3 * (i + 1);
   auto step = [&](int u, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool at_end = HEADS == 2 && MASKED && hsel == 0;
     if (!at_end && u + 1 < nsub) issue_loads(u + 1, knext, vnext);
     compute(u, kcur, vcur);
     if (at_end && u + 1 < nsub) issue_loads(u + 1, knext, vnext);
