@@ -18,10 +18,7 @@
 //  * S^T = K Q^T (v_mfma_f32_32x32x16_bf16): K operand = one ds_read_b128 per MFMA.  O^T = V^T P^T: the V^T
 //    operand is gathered from the row-major V tile by two ds_read_b64_tr_b16 (transposing 16-bit reads),
 //    in the key order that the S^T accumulator layout gives P^T, so P never moves between lanes.
-//  * softmax: the Q fragments are multiplied by scale * log2(e) once, when they are loaded (rounded back
-//    to bf16: a relative change of at most 2^-9 per element, below the rounding of P itself), and the
-//    S^T accumulators start from -m_run instead of zero, so each P is one raw v_exp_f32 (no denormal
-//    fix-up) of an accumulator, with no vector instruction between the MFMAs and the exponentials.
+//  * softmax: raw v_exp_f32 (no denormal fix-up) of one FMA that folds the scale and the reference max.
 //    There is no per-tile row max: the reference is taken from the first visible keys of each row and
 //    kept while a tile's sum of P stays <= 2^32 (bf16 and fp32 have the same exponent range, so P keeps
 //    its relative precision at any scale); a larger sum (or inf) recomputes the tile's scores, moves
@@ -37,8 +34,6 @@
 //    loads feeds twice the MFMA work and each wave issues half the loads.  The list is the union of the
 //    two mask rows, each entry carrying one selection bit per head; a wave skips the compute of a block its
 //    head did not select (the heads of a KV group select nearly the same blocks).
-#include <type_traits>
-
 #include "stem_internal.h"
 
 namespace stem {
@@ -175,16 +170,11 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
   const bool qvalid = qpos < L;
   bf16x8 qf[8];
   {
-    const float cq = a.scale_log2;  // scores come out in log2 units
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)(tb + qpos) * a.hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       uint4 w = qvalid ? *(const uint4*)(qp + 16 * kk + 8 * half) : make_uint4(0u, 0u, 0u, 0u);
-      uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        ww[t] = cvt_bf16x2(__uint_as_float(ww[t] << 16) * cq, __uint_as_float(ww[t] & 0xFFFF0000u) * cq);
-      qf[kk] = __builtin_bit_cast(bf16x8, make_uint4(ww[0], ww[1], ww[2], ww[3]));
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -296,9 +286,7 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
     for (int x = 0; x < 16; ++x) o[dt][x] = 0.f;
   float m_run = -1e30f;  // reference max (log2 units); finite so masked rows never form inf - inf
   float l_part = 0.f;
-  f32x16 cm;  // -m_run in every entry: the first S^T MFMA of a sub-tile takes it as its C operand
-#pragma unroll
-  for (int x = 0; x < 16; ++x) cm[x] = 0.f;
+  const float c2 = a.scale_log2;
 
   // The compute of sub-tile u (K and V in kcur, vcur).
   auto compute = [&](int u, const uint8_t* kcur, const uint8_t* vcur) __attribute__((always_inline)) {
@@ -312,11 +300,12 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
     const lds_u8* Kt = (const lds_u8*)kcur;
     const lds_u8* Vt = (const lds_u8*)vcur;
     f32x16 s0, s1;
-    auto scores = [&](auto zc) {
-      constexpr bool Z = decltype(zc)::value;
-      f32x16 c0;
+    auto scores = [&]() {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) c0[x] = 0.f;
+      for (int x = 0; x < 16; ++x) {
+        s0[x] = 0.f;
+        s1[x] = 0.f;
+      }
       // K fragments are read two k-steps ahead of the MFMAs that use them (hides the LDS latency)
       bf16x8 ka[3], kb[3];
 #pragma unroll
@@ -332,8 +321,8 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
           kb[(kk + 2) % 3] = *(const __attribute__((address_space(3))) bf16x8*)(Kt + koffs[kk + 2] + 32 * 256);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3], qf[kk], kk ? s0 : Z ? c0 : cm, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3], qf[kk], kk ? s1 : Z ? c0 : cm, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % 3], qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk % 3], qf[kk], s1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (diag) {
@@ -359,7 +348,7 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
       mx = fmaxf(mx, s1[15]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run, mx * c2);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_part *= alpha;
 #pragma unroll
@@ -367,19 +356,15 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
 #pragma unroll
         for (int x = 0; x < 16; ++x) o[dt][x] *= alpha;
       m_run = m_new;
-#pragma unroll
-      for (int x = 0; x < 16; ++x) cm[x] = -m_new;
     };
     uint4 pw[4];  // P rounded to bf16 pairs, the B operand of each k-step
-    // P = 2^(s - m_run), packed; returns the sum of the rounded values (v_dot2_f32_bf16 with (1, 1)).
-    // Z (first visible keys or a rebase): the accumulators hold s, else s - m_run already.
-    auto exp_pack = [&](auto zc) -> float {
-      constexpr bool Z = decltype(zc)::value;
+    // P = 2^(s c2 - m_run), packed; returns the sum of the rounded values (v_dot2_f32_bf16 with (1, 1)).
+    auto exp_pack = [&]() -> float {
       const float negm = -m_run;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        s0[x] = __builtin_amdgcn_exp2f(Z ? s0[x] + negm : s0[x]);
-        s1[x] = __builtin_amdgcn_exp2f(Z ? s1[x] + negm : s1[x]);
+        s0[x] = __builtin_amdgcn_exp2f(fmaf(s0[x], c2, negm));
+        s1[x] = __builtin_amdgcn_exp2f(fmaf(s1[x], c2, negm));
       }
       const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
       float ps0 = 0.f, ps1 = 0.f;
@@ -403,15 +388,10 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
     float ps;
     for (;;) {
       asm volatile("" ::: "memory");  // keep the K reads inside the (rarely repeated) loop body
-      if (force) {
-        scores(std::true_type{});
-        rebase();
-        ps = exp_pack(std::true_type{});
-        break;
-      }
-      scores(std::false_type{});
-      ps = exp_pack(std::false_type{});
-      if (__ballot(!(ps <= kOverflow)) == 0) break;
+      scores();
+      if (force) rebase();
+      ps = exp_pack();
+      if (force || __ballot(!(ps <= kOverflow)) == 0) break;
       force = true;
     }
     l_part += ps;

@@ -246,6 +246,56 @@ def test_dense_mode_matches_textbook_attention(dev, name, over):
     assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
 
 
+LARGE = [("llama_32k_bf16", dict(lens=(1000, 300), hq=4, hkv=2)),
+         ("llama_32k_bf16", dict(lens=(700,), hq=3, hkv=1)),
+         ("w8a8_128k_fp8", dict(lens=(1000, 300), hq=4, hkv=2)),
+         ("tiny_f32", dict(lens=(600,), hq=4, hkv=2))]
+
+
+@pytest.mark.parametrize("factor", [2.0, 4.0, 8.0])
+@pytest.mark.parametrize("name,over,dense", [(n, o, False) for n, o in LARGE] + [(*LARGE[0], True)],
+                         ids=["bf16", "bf16-one-head-per-workgroup", "fp8", "f32", "bf16-dense"])
+def test_large_logits_take_the_rebase_path(dev, name, over, dense, factor):
+    """Q and K scaled by an exact power of two, so every logit grows by factor^2 (at 8: logits up to ~200,
+    row spreads of ~40 in natural units): rows get peaked and later keys outgrow the softmax reference
+    taken from a row's first keys by more than the 2^32 the kernels allow, which sends them through
+    their recompute-and-rebase path.
+
+    Tolerances for these inputs, derived: the logits are exact fp32 sums of exact products, so their
+    magnitude adds no error; each P is rounded to bf16 (2^-9 relative) and the row sum adds the same
+    rounded values, so the output is a mean of V under weights perturbed by at most 2^-8 relative, an
+    error of at most 2^-8 times the spread of V about the output (max |v| bounds it here, with the
+    worst case's factor 2 dropped: the perturbations do not all take their extremes) or the dtype's
+    tolerance, whichever is larger; the LSE moves by at most ~2^-9 (checked at 1e-2).  The fp32 path
+    keeps P in fp32; its logits' rounding is relative, so its tolerance grows with them (factor^2)."""
+    p = synth.make_problem(name, **over)
+    _log(f"[large logits] {name} {over} x{factor} dense={dense}")
+    x = synth.make_inputs(p, seed=6)
+    f = np.float32(factor)
+    if p.dtype == "fp8":  # the codes stay, the per-head scales grow
+        x["q_scale"] = x["q_scale"] * f
+        x["k_scale"] = x["k_scale"] * f
+    elif p.dtype == "bf16":  # exact: a power of two moves the exponent only
+        for key in ("q", "k"):
+            x[key] = synth.bf16_bits((x[key].astype(np.uint32) << 16).view(np.float32) * f)
+    else:
+        x["q"], x["k"] = x["q"] * f, x["k"] * f
+    if dense:
+        g = _run(p, x, dev, dense=True)
+        ora = sc.oracle_attention(p, x, None)
+    else:
+        ref1 = sc.oracle_stage1(p, x)
+        masks = sc.oracle_masks([s for *_, s in ref1], sc.oracle_budgets(p))
+        g = _run(p, x, dev, masks_for_bsa=masks)
+        ora = sc.oracle_attention(p, x, masks)
+    mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
+    vmax = max(float(np.abs(sc.decode_kv(p, x, r, "v")).max()) for r in range(len(p.lens)) if p.lens[r] > 0)
+    tmax, tmean = sc.TOL[p.dtype]
+    bound = max(tmax, 2.0 ** -8 * vmax) if p.dtype != "f32" else tmax * factor ** 2
+    _log(f"  out max {mx:.2e} (bound {bound:.2e}) mean {mean:.2e} lse {lerr:.2e}")
+    assert mx <= bound and mean <= tmean and lerr <= 1e-2
+
+
 def test_end_to_end_gpu_selection_feeds_attention(dev):
     p = synth.make_problem("llama_32k_bf16", lens=(1200, 333), hq=8, hkv=2)
     x = synth.make_inputs(p, seed=2)
