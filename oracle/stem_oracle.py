@@ -29,8 +29,9 @@ Readings of points the pages leave open (each one is listed, with its reason, in
 Parity pins (tests under `tests/`, marked "not gpu"): every function below is pinned by something other
 than itself -- brute-force token-level scores, an independent floating-point bisection of the TPD solve,
 a brute-force selection by Python sorting, textbook dense causal attention via torch's CPU SDPA routine at
-a 100% budget and with an additive -inf mask, the e4m3fn / bf16 decodes against torch's casts, and the
-paged gather against the contiguous layout.  No function is "parity unpinned".
+a 100% budget and with an additive -inf mask, the e4m3fn / bf16 decodes against torch's casts, the fp8
+dequantisation against hand-built codes under distinct per-head scales and against torch's decode times
+the scale, and the paged gather against the contiguous layout.  No function is "parity unpinned".
 """
 from __future__ import annotations
 

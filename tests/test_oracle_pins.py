@@ -406,11 +406,43 @@ def test_quantize_fp8_per_head_closed_forms():
     assert scale[1] == np.float32(np.float32(12.5) / np.float32(448.0))
     assert codes[7, 1, 3] == 0x7E and codes[9, 1, 4] == (0x80 | 0x76)  # 448 = 1.75*2^8, 224 = 1.75*2^7
     back = oracle.fp8_to_f64(codes, scale)
-    tab = oracle.e4m3fn_table()
     for h in range(3):
+        # the dequantised value is within half a quantum of x, in x's own units: the quantum of y = x/scale
+        # (2^-3 of y's binade, 2^-9 below the normal range) times the head's scale
         y = x[:, h] / float(scale[h])
-        q = tab[codes[:, h] & 0x7F]
         e = np.maximum(np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))), -6).astype(np.int64)
-        spacing = np.ldexp(1.0, np.minimum(e, 8) - 3)
-        assert np.all(np.abs(np.abs(y) - q) <= spacing / 2 + 1e-12)
-    assert np.all(np.isfinite(back))
+        spacing = np.ldexp(1.0, np.minimum(e, 8) - 3) * float(scale[h])
+        assert np.all(np.abs(back[:, h] - x[:, h]) <= spacing / 2 * (1 + 1e-9))
+
+
+def test_fp8_dequantisation_applies_each_heads_own_scale():
+    """W8A8 dequantisation ([Arch] "答案不在算法里", W8A8-FP8): value = e4m3fn(code) * scale[head].
+    Hand-built codes with exact values (0x38 = 1.0, 0xB0 = -0.5, 0x7E = 448, 0x01 = 2^-9) under three
+    distinct per-head scales: dividing by the scale, dropping it or taking another head's scale all fail."""
+    scale = np.array([0.5, 2.0, 3.0], dtype=np.float32)
+    codes = np.zeros((2, 3, 4), dtype=np.uint8)
+    codes[:, :, 0] = 0x38
+    codes[:, :, 1] = 0xB0
+    codes[:, :, 2] = 0x7E
+    codes[:, :, 3] = 0x01
+    back = oracle.fp8_to_f64(codes, scale)
+    unit = np.array([1.0, -0.5, 448.0, 2.0 ** -9])
+    for t in range(2):
+        for h in range(3):
+            assert np.array_equal(back[t, h], unit * float(scale[h])), (t, h)
+    # a single head slice with its own one-element scale array, as the tests pass it
+    assert np.array_equal(oracle.fp8_to_f64(codes[:, 2:3], scale[2:3])[0, 0], unit * 3.0)
+
+
+def test_fp8_dequantisation_matches_torch_decode_times_scale():
+    """Random codes of every finite value, four heads with unrelated scales: the oracle's dequantisation
+    equals torch's float8_e4m3fn decode multiplied by the head's scale, exactly (both are exact in
+    float64)."""
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, size=(257, 4, 16), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11  # NaN codes aside
+    scale = np.array([1.5e-3, 0.75, 7.0, 2.0 ** -20], dtype=np.float32)
+    got = oracle.fp8_to_f64(codes, scale)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = dec * scale.astype(np.float64)[None, :, None]
+    assert np.array_equal(got, want)
