@@ -12,6 +12,11 @@ import oracle
 # 2^-24 relative per term; 1e-4 max / 1e-5 mean keeps a wide margin on outputs of magnitude ~1).
 TOL = {"bf16": (2e-2, 2e-3), "fp8": (6e-2, 6e-3), "f32": (1e-4, 1e-5)}
 TIE_REL = 1e-5  # near-tie window for selection
+# LSE bound, derived: the attention kernels round each P to bf16 (relative error <= 2^-9) and their row
+# sums add those rounded values, so the sum moves by at most 2^-9 relative and the LSE by at most
+# ln(1 + 2^-9) ~ 1.95e-3 (fp32 accumulation adds ~1e-6; the fp32 kernel keeps P in fp32).  1e-2 leaves a
+# factor of 5 and still fails an LSE that is off by a visible amount.
+LSE_TOL = 1e-2
 
 
 def request_slices(p):
@@ -153,14 +158,32 @@ def compare_attention(p, oracle_res, gpu_out, gpu_lse, rows_per_req=None):
     return float(e.max()), float(e.mean()), float(le.max() if le.size else 0.0)
 
 
-def sample_rows(p, r, count, seed=0):
-    """Rows (h, i) to check at full size: first/last heads, first/middle/last blocks, plus random ones."""
+def sample_rows(p, r, extra, seed=0, mask=None):
+    """Rows (h, i) to check at full size: first/middle/last heads at the first, middle and last blocks;
+    the rows around the end of the TPD plan's capped prefix (the last rows with k_i = i + 1 and the first
+    ones below it); with `mask` (request r's bool [hq][n][n] selection), the rows where the union of two
+    consecutive heads' selections crosses 3/4 of the row's causal blocks (the attention kernel changes
+    when it issues its tile loads there); then `extra` random rows."""
     n = p.nblocks(r)
     rng = np.random.default_rng(seed + r)
     hs = sorted({0, p.hq // 2, p.hq - 1})
-    is_ = sorted({0, 1 % n, n // 3, n // 2, max(n - 2, 0), n - 1})
-    rows = {(h, i) for h in hs for i in is_}
-    while len(rows) < count:
+    is_ = {0, 1 % n, n // 3, n // 2, max(n - 2, 0), n - 1}
+    k = oracle.tpd_budgets(n, p.rho_num, p.rho_den, p.mu_num, p.mu_den)
+    below = np.nonzero(k < np.arange(1, n + 1))[0]
+    if below.size:
+        c = int(below[0])  # first row whose budget is below its causal block count
+        is_ |= {i for i in (c - 2, c - 1, c, c + 1) if 0 <= i < n}
+    rows = {(h, i) for h in hs for i in sorted(is_)}
+    if mask is not None and p.hq >= 2:
+        for h in (0, (p.hq // 2) & ~1):
+            union = (mask[h] | mask[h + 1]).sum(axis=1)
+            fits = 4 * union <= 3 * (np.arange(n) + 1)
+            flips = np.nonzero(fits[1:] != fits[:-1])[0]
+            if flips.size:
+                f = int(flips[0]) + 1  # first row on the other side of the switch
+                rows |= {(hh, i) for hh in (h, h + 1) for i in (f - 1, f) if 0 <= i < n}
+    want = len(rows) + extra
+    while len(rows) < want:
         rows.add((int(rng.integers(p.hq)), int(rng.integers(n))))
     return sorted(rows)
 

@@ -142,7 +142,7 @@ def test_small_case_all_outputs(dev, name, over):
     tmax, tmean = sc.TOL[p.dtype]
     _log(f"  score rel err {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
     assert mx <= tmax and mean <= tmean
-    assert lerr <= 10 * tmax
+    assert lerr <= sc.LSE_TOL
 
 
 def _random_problem(seed):
@@ -189,7 +189,7 @@ def test_random_small_problem_all_outputs(dev, seed):
     tmax, tmean = sc.TOL[p.dtype]
     _log(f"  near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
     assert mx <= tmax and mean <= tmean
-    assert lerr <= 10 * tmax
+    assert lerr <= sc.LSE_TOL
 
 
 def test_plain_c_program_runs_the_path(dev, tmp_path):
@@ -229,7 +229,7 @@ def test_plain_c_program_runs_the_path(dev, tmp_path):
     ora = sc.oracle_attention(p, x, [gmask])
     mx, mean, lerr = sc.compare_attention(p, ora, out, lse)
     _log(f"  out max {mx:.2e} mean {mean:.2e} lse {lerr:.2e}")
-    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= 0.2
+    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= sc.LSE_TOL
 
 
 @pytest.mark.parametrize("name,over", [SMALL[0], SMALL[2], SMALL[3], SMALL[9], SMALL[11]],
@@ -243,7 +243,7 @@ def test_dense_mode_matches_textbook_attention(dev, name, over):
     mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
     _log(f"[dense] {name}: out max {mx:.2e} mean {mean:.2e} lse {lerr:.2e}")
     tmax, tmean = sc.TOL[p.dtype]
-    assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+    assert mx <= tmax and mean <= tmean and lerr <= sc.LSE_TOL
 
 
 LARGE = [("llama_32k_bf16", dict(lens=(1000, 300), hq=4, hkv=2)),
@@ -255,19 +255,59 @@ LARGE = [("llama_32k_bf16", dict(lens=(1000, 300), hq=4, hkv=2)),
 @pytest.mark.parametrize("factor", [2.0, 4.0, 8.0])
 @pytest.mark.parametrize("name,over,dense", [(n, o, False) for n, o in LARGE] + [(*LARGE[0], True)],
                          ids=["bf16", "bf16-one-head-per-workgroup", "fp8", "f32", "bf16-dense"])
+def _bf16_round(a):
+    """float64 -> nearest bf16 value (through float32, ties to even), as float64."""
+    u = np.asarray(a, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _bf16_p_model_error(p, x, masks, ora):
+    """Max abs error, against the oracle, of a model of the kernels' rounding (test-side, not part of the
+    oracle): float64 attention whose softmax weights P are rounded to bf16 before they weight V and before
+    they are summed, with the output rounded to bf16.  Only the reference point of the exponentials differs
+    from the kernels (the row max here), which changes which way each P rounds but not by how much."""
+    worst = 0.0
+    grp = p.hq // p.hkv
+    scale = 1.0 / math.sqrt(p.d)
+    for r, (a, b) in enumerate(sc.request_slices(p)):
+        L, n = b - a, p.nblocks(r)
+        if L == 0:
+            continue
+        q, k, v = sc.decode_q(p, x, a, b), sc.decode_kv(p, x, r, "k"), sc.decode_kv(p, x, r, "v")
+        m = masks[r] if masks is not None else np.ones((p.hq, n, n), dtype=bool)
+        O = ora[r][0]
+        for h in range(p.hq):
+            for i in range(n):
+                t0, t1 = i * p.block, min((i + 1) * p.block, L)
+                sel = np.nonzero(m[h, i, : i + 1])[0]
+                if not len(sel):
+                    continue
+                kid = np.concatenate([np.arange(j * p.block, min((j + 1) * p.block, L)) for j in sel])
+                lg = q[t0:t1, h] @ k[kid, h // grp].T * scale
+                lg = np.where(kid[None, :] <= np.arange(t0, t1)[:, None], lg, -np.inf)
+                P = _bf16_round(np.exp(lg - lg.max(axis=1, keepdims=True)))
+                o = _bf16_round((P @ v[kid, h // grp]) / P.sum(axis=1, keepdims=True))
+                worst = max(worst, float(np.abs(o - O[t0:t1, h]).max()))
+    return worst
+
+
+@pytest.mark.parametrize("factor", [2.0, 4.0, 8.0])
+@pytest.mark.parametrize("name,over,dense", [(n, o, False) for n, o in LARGE] + [(*LARGE[0], True)],
+                         ids=["bf16", "bf16-one-head-per-workgroup", "fp8", "f32", "bf16-dense"])
 def test_large_logits_take_the_rebase_path(dev, name, over, dense, factor):
     """Q and K scaled by an exact power of two, so every logit grows by factor^2 (at 8: logits up to ~200,
     row spreads of ~40 in natural units): rows get peaked and later keys outgrow the softmax reference
-    taken from a row's first keys by more than the 2^32 the kernels allow, which sends them through
-    their recompute-and-rebase path.
+    taken from a row's first keys by more than the kernels allow, which sends them through their rebase
+    path.
 
-    Tolerances for these inputs, derived: the logits are exact fp32 sums of exact products, so their
-    magnitude adds no error; each P is rounded to bf16 (2^-9 relative) and the row sum adds the same
-    rounded values, so the output is a mean of V under weights perturbed by at most 2^-8 relative, an
-    error of at most 2^-8 times the spread of V about the output (max |v| bounds it here, with the
-    worst case's factor 2 dropped: the perturbations do not all take their extremes) or the dtype's
-    tolerance, whichever is larger; the LSE moves by at most ~2^-9 (checked at 1e-2).  The fp32 path
-    keeps P in fp32; its logits' rounding is relative, so its tolerance grows with them (factor^2)."""
+    Bound, computed: the logits are exact fp32 sums of exact products, so their size adds no error; what
+    peaked rows expose is the bf16 rounding of each P and of the output.  A float64 model with exactly
+    those roundings (_bf16_p_model_error) gives the error they cause on these inputs; the kernel must stay
+    within 1.5x of it (it rounds other P values, since its exponentials start from another reference, so
+    its maximum is another draw of the same size) or within the dtype's tolerance, whichever is larger.
+    The fp32 path keeps P in fp32; its logits' rounding is relative, so its tolerance grows with them
+    (factor^2)."""
     p = synth.make_problem(name, **over)
     _log(f"[large logits] {name} {over} x{factor} dense={dense}")
     x = synth.make_inputs(p, seed=6)
@@ -281,19 +321,22 @@ def test_large_logits_take_the_rebase_path(dev, name, over, dense, factor):
     else:
         x["q"], x["k"] = x["q"] * f, x["k"] * f
     if dense:
+        masks = None
         g = _run(p, x, dev, dense=True)
-        ora = sc.oracle_attention(p, x, None)
     else:
         ref1 = sc.oracle_stage1(p, x)
         masks = sc.oracle_masks([s for *_, s in ref1], sc.oracle_budgets(p))
         g = _run(p, x, dev, masks_for_bsa=masks)
-        ora = sc.oracle_attention(p, x, masks)
+    ora = sc.oracle_attention(p, x, masks)
     mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"])
-    vmax = max(float(np.abs(sc.decode_kv(p, x, r, "v")).max()) for r in range(len(p.lens)) if p.lens[r] > 0)
     tmax, tmean = sc.TOL[p.dtype]
-    bound = max(tmax, 2.0 ** -8 * vmax) if p.dtype != "f32" else tmax * factor ** 2
-    _log(f"  out max {mx:.2e} (bound {bound:.2e}) mean {mean:.2e} lse {lerr:.2e}")
-    assert mx <= bound and mean <= tmean and lerr <= 1e-2
+    if p.dtype == "f32":
+        model, bound = 0.0, tmax * factor ** 2
+    else:
+        model = _bf16_p_model_error(p, x, masks, ora)
+        bound = max(tmax, 1.5 * model)
+    _log(f"  out max {mx:.2e} (bf16-P model {model:.2e}, bound {bound:.2e}) mean {mean:.2e} lse {lerr:.2e}")
+    assert mx <= bound and mean <= tmean and lerr <= sc.LSE_TOL
 
 
 def test_end_to_end_gpu_selection_feeds_attention(dev):
@@ -365,14 +408,14 @@ def test_full_size_workload(dev, name):
     g = _run(p, x, dev, masks_for_bsa=masks)
     worst = _check_stage1(p, g, ref1)
     ties = sc.check_selection(p, S_list, budgets, g["words"], g["counts"])
-    rows = [sc.sample_rows(p, r, 12) if p.lens[r] > 4096 else None for r in range(len(p.lens))]
+    rows = [sc.sample_rows(p, r, 12, mask=masks[r]) if p.lens[r] > 4096 else None for r in range(len(p.lens))]
     _log(f"[full] {name}: oracle attention on sampled rows")
     ora = sc.oracle_attention(p, x, masks, rows)
     mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
     _log(f"[full] {name}: score rel {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, "
          f"lse {lerr:.2e}")
     tmax, tmean = sc.TOL[p.dtype]
-    assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+    assert mx <= tmax and mean <= tmean and lerr <= sc.LSE_TOL
 
 
 # ------------------------------------------------------------------------------------ W8A8 quantising stage 1
@@ -604,7 +647,7 @@ def test_inloop_variant_equals_list_variant_and_oracle(dev, lens, hq, hkv, rho):
     ora = sc.oracle_attention(p, x, gm)
     mx, mean, lerr = sc.compare_attention(p, ora, o2.float().cpu().numpy().astype(np.float64),
                                           l2.cpu().numpy().astype(np.float64))
-    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= 0.2
+    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= sc.LSE_TOL
 
 
 def test_inloop_variant_external_mask_with_empty_rows(dev):
@@ -654,12 +697,12 @@ def test_ablation_switches_full_size_32k(dev, over):
     g = _run(p, x, dev, masks_for_bsa=masks)
     worst = _check_stage1(p, g, ref1)
     ties = sc.check_selection(p, S_list, budgets, g["words"], g["counts"])
-    rows = [sc.sample_rows(p, 0, 8)]
+    rows = [sc.sample_rows(p, 0, 8, mask=masks[0])]
     ora = sc.oracle_attention(p, x, masks, rows)
     mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
     _log(f"  score rel {worst:.2e}, near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
     tmax, tmean = sc.TOL[p.dtype]
-    assert mx <= tmax and mean <= tmean and lerr <= 10 * tmax
+    assert mx <= tmax and mean <= tmean and lerr <= sc.LSE_TOL
 
 
 # ------------------------------------------------------------------------------------ maximum sizes
@@ -678,11 +721,11 @@ def test_longest_request_the_masked_kernels_take(dev):
     g = _run(p, x, dev, masks_for_bsa=masks)
     _check_stage1(p, g, ref1)
     ties = sc.check_selection(p, S_list, budgets, g["words"], g["counts"])
-    rows = [sc.sample_rows(p, 0, 6)]
+    rows = [sc.sample_rows(p, 0, 6, mask=masks[0])]
     ora = sc.oracle_attention(p, x, masks, rows)
     mx, mean, lerr = sc.compare_attention(p, ora, g["out"], g["lse"], rows)
     _log(f"[max] near-tie rows {ties}, out max {mx:.2e} mean {mean:.2e}, lse {lerr:.2e}")
-    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= 0.2
+    assert mx <= 2e-2 and mean <= 2e-3 and lerr <= sc.LSE_TOL
     L, m1, c1 = _fused_vs_two_stage(p, x, dev)
     assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
 
