@@ -215,7 +215,12 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_bf16_kernel(BsaArg
       return (uint32_t)(u >> 1) | kSelFirst | kSelSecond;
     }
   };
-  auto sub_key0 = [&](uint32_t e, int u) -> int { return (int)(e & kBlockBits) * B + (u & 1) * KT; };
+  // first key of sub-tile u; only list entries pack the block index (dense and in-loop steps walk j = u/2,
+  // which may exceed the list's 14 bits)
+  auto sub_key0 = [&](uint32_t e, int u) -> int {
+    const int j = (MASKED && !INLOOP) ? (int)(e & kBlockBits) : (u >> 1);
+    return j * B + (u & 1) * KT;
+  };
   // must the workgroup load sub-tile u (in-loop variant: is its block selected by any head)?
   auto wanted = [&](uint32_t e) -> bool { return !INLOOP || (e & (kSelFirst | kSelSecond)) != 0; };
 

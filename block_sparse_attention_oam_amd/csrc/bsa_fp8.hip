@@ -176,7 +176,12 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
     if constexpr (MASKED) return (uint32_t)list[u >> 1];
     else return (uint32_t)(u >> 1) | kSelFirst | kSelSecond;
   };
-  auto sub_key0 = [&](uint32_t e, int u) -> int { return (int)(e & kBlockBits) * B + (u & 1) * KT; };
+  // first key of sub-tile u; only list entries pack the block index (dense steps walk j = u/2, which may
+  // exceed the list's 14 bits)
+  auto sub_key0 = [&](uint32_t e, int u) -> int {
+    const int j = MASKED ? (int)(e & kBlockBits) : (u >> 1);
+    return j * B + (u & 1) * KT;
+  };
   auto key_row_off = [&](int kp) -> int64_t {
     if (PAGE == 0) return ((int64_t)tb + kp) * row_stride + head_off;
     const int page = a.kv.page_table[(int64_t)r * a.kv.pt_stride + kp / a.kv.page_size];

@@ -730,6 +730,45 @@ def test_longest_request_the_masked_kernels_take(dev):
     assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama_128k_bf16", "w8a8_128k_fp8"], ids=["bf16", "fp8"])
+def test_dense_mode_beyond_16384_blocks(dev, name):
+    """Dense causal attention (no mask) of one request of 16400 blocks (2,099,200 tokens), two query heads
+    of one KV head: the rows of blocks 16383, 16384 and 16399, which see keys in blocks past 2^14, against
+    the oracle.  (Masked calls stop at 2048 blocks; the dense walk has no such limit.)"""
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    p = synth.make_problem(name, lens=(16400 * 128,), hq=2, hkv=1)
+    _log(f"[dense 16400 blocks] {name}: generating inputs")
+    x = synth.make_inputs(p, seed=8)
+    kw = {}
+    if p.dtype == "fp8":
+        kw = dict(q_scale=upload(x["q_scale"]), k_scale=upload(x["k_scale"]), v_scale=upload(x["v_scale"]))
+    prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype, **kw)
+    q, k, v = upload(x["q"]), upload(x["k"]), upload(x["v"])
+    L = StemPrefill(prob, dev)
+    _log(f"[dense 16400 blocks] {name}: GPU run")
+    L.attend(q, k, v, mask=None)
+    torch.cuda.synchronize()
+    rows = [(0, 16383), (1, 16384), (0, 16399), (1, 16399)]
+    out = np.empty(L.out.shape, dtype=np.float64)
+    lse = np.full(L.lse.shape, np.nan)
+    for h, i in rows:
+        sl = slice(i * p.block, (i + 1) * p.block)
+        out[sl, h] = L.out[sl, h].float().cpu().numpy()
+        lse[h, sl] = L.lse[h, sl].cpu().numpy()
+    del q, k, v, L
+    torch.cuda.empty_cache()
+    n = p.nblocks(0)
+    _log(f"[dense 16400 blocks] {name}: oracle rows")
+    ora = sc.oracle_attention(p, x, [np.broadcast_to(np.bool_(True), (p.hq, n, n))], [rows])
+    mx, mean, lerr = sc.compare_attention(p, ora, out, lse, [rows])
+    _log(f"  out max {mx:.2e} mean {mean:.2e} lse {lerr:.2e}")
+    tmax, tmean = sc.TOL[p.dtype]
+    assert mx <= tmax and mean <= tmean and lerr <= sc.LSE_TOL
+
+
 # ------------------------------------------------------------------------------------ budgets on the device
 BUDGET_SWEEP = [(n, rho, mu) for n in (1, 2, 3, 5, 12, 31, 32, 33, 64, 65, 100, 255, 256, 1000, 1024, 2048, 4096)
                 for rho in ((25, 100), (10, 100), (50, 100), (100, 100), (1, 100), (1, 3))
