@@ -23,11 +23,12 @@ STEM_E_HIP = -4
 
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 MAX_REQS = 256
+SCRATCH_BYTES = 64 << 20  # STEM_SCRATCH_BYTES
 
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
            "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
            "bsa_prefill_inloop", "stem_score_select", "stem_naive_workspace_bytes", "stem_naive_score",
-           "stem_quantize_score"]
+           "stem_quantize_score", "stem_score_noalloc"]
 
 
 class StemError(RuntimeError):
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.stem_last_error.argtypes = []
         L.stem_last_error.restype = ctypes.c_char_p
         L.stem_score.argtypes = [P, vp, vp, vp, ctypes.c_float, vp, i64, vp, sz, vp]
+        L.stem_score_noalloc.argtypes = [P, vp, vp, vp, ctypes.c_float, vp, i64, vp]
         L.stem_tpd_topk.argtypes = [P, vp, i64, i32, i32, i32, i32, vp, i32, vp, vp]
         L.bsa_prefill.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
@@ -88,7 +90,8 @@ def lib() -> ctypes.CDLL:
         L.stem_naive_workspace_bytes.restype = sz
         L.stem_naive_score.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, vp, i64, vp, sz, vp, sz, vp]
         for name in ("stem_block_counts", "stem_workspace_layout", "stem_tpd_budgets_host", "stem_score",
-                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select", "stem_naive_score", "stem_quantize_score"):
+                     "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select", "stem_naive_score", "stem_quantize_score",
+                     "stem_score_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,6 +186,12 @@ def stem_score(p: Problem, q, k, v, beta: float, scores, ws, stream=None) -> Non
     _check(lib().stem_score(p.ref, _ptr(q), _ptr(k), _ptr(v), float(beta), _ptr(scores),
                             int(scores.shape[-1]), _ptr(ws), int(ws.numel() * ws.element_size()),
                             _stream(stream)))
+
+
+def stem_score_noalloc(p: Problem, q, k, v, beta: float, scores, stream=None) -> None:
+    """stem_score with the pooled tensors in the library's static per-device scratch (no workspace)."""
+    _check(lib().stem_score_noalloc(p.ref, _ptr(q), _ptr(k), _ptr(v), float(beta), _ptr(scores),
+                                    int(scores.shape[-1]), _stream(stream)))
 
 
 def stem_tpd_topk(p: Problem, scores, rho: tuple, mu: tuple, mask, counts, stream=None) -> None:

@@ -130,6 +130,31 @@ int check_device() {
   return STEM_OK;
 }
 
+// ---- static scratch of stem_score_noalloc: the pooled q-bar, k-bar and M of its calls live here instead of
+// in a caller workspace.  One copy per device (the code object's global), held until the process ends.  In
+// host code `scratch` is only a stand-in for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device and kept.
+static __device__ __align__(256) uint8_t scratch[STEM_SCRATCH_BYTES];
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device id; nullptr until looked up
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(STEM_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(STEM_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return STEM_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(STEM_E_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -258,23 +283,13 @@ static hipError_t launch_pooling(const stem_problem* p, const Plan& pl, const vo
   return launch_pool(pa, p->dtype, s);
 }
 
-int stem_score(const stem_problem* p, const void* q, const void* k, const void* v, float beta, float* scores,
-               int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream) {
-  Plan pl;
-  int st = make_plan(p, &pl);
-  if (st != STEM_OK) return st;
-  if (!scores) return fail(STEM_E_INVALID_ARG, "q, k, v and scores must be non-NULL");
-  if (score_row_stride < pl.max_n)
-    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d blocks of the longest request",
-                (long long)score_row_stride, pl.max_n);
-  st = check_pool_args(p, pl, q, k, v, beta, ws, ws_bytes);
-  if (st != STEM_OK) return st;
-  st = check_device();
-  if (st != STEM_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
+}  // extern "C"
+
+// The launches of stem_score (pooling into ws, then the scoring GEMM), after validation.
+static int launch_score_stage(const stem_problem* p, const Plan& pl, const void* q, const void* k, const void* v,
+                              float beta, float* scores, int64_t score_row_stride, void* ws, hipStream_t s) {
   hipError_t e = launch_pooling(p, pl, q, k, v, ws, s);
   if (e != hipSuccess) return hip_status(e, "pool launch");
-
   size_t oq, okk, om, need;
   layout(pl, &oq, &okk, &om, &need);
   ScoreArgs sa;
@@ -292,6 +307,49 @@ int stem_score(const stem_problem* p, const void* q, const void* k, const void* 
   sa.rt = pl.rt;
   e = launch_score(sa, pl.max_n, p->num_reqs, s);
   return hip_status(e, "score launch");
+}
+
+extern "C" {
+
+int stem_score(const stem_problem* p, const void* q, const void* k, const void* v, float beta, float* scores,
+               int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  if (!scores) return fail(STEM_E_INVALID_ARG, "q, k, v and scores must be non-NULL");
+  if (score_row_stride < pl.max_n)
+    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d blocks of the longest request",
+                (long long)score_row_stride, pl.max_n);
+  st = check_pool_args(p, pl, q, k, v, beta, ws, ws_bytes);
+  if (st != STEM_OK) return st;
+  st = check_device();
+  if (st != STEM_OK) return st;
+  return launch_score_stage(p, pl, q, k, v, beta, scores, score_row_stride, ws, (hipStream_t)stream);
+}
+
+int stem_score_noalloc(const stem_problem* p, const void* q, const void* k, const void* v, float beta,
+                       float* scores, int64_t score_row_stride, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  if (!scores) return fail(STEM_E_INVALID_ARG, "q, k, v and scores must be non-NULL");
+  if (score_row_stride < pl.max_n)
+    return fail(STEM_E_INVALID_ARG, "score_row_stride = %lld < %d blocks of the longest request",
+                (long long)score_row_stride, pl.max_n);
+  size_t oq, okk, om, need;
+  layout(pl, &oq, &okk, &om, &need);
+  if (need > (size_t)STEM_SCRATCH_BYTES)
+    return fail(STEM_E_UNSUPPORTED, "this problem pools %zu bytes; the static scratch of stem_score_noalloc holds "
+                "%zu (use stem_score with a workspace)", need, (size_t)STEM_SCRATCH_BYTES);
+  // the scratch is 256-byte aligned and large enough: validate the rest as stem_score does
+  st = check_pool_args(p, pl, q, k, v, beta, (void*)(uintptr_t)256, (size_t)STEM_SCRATCH_BYTES);
+  if (st != STEM_OK) return st;
+  st = check_device();
+  if (st != STEM_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != STEM_OK) return st;
+  return launch_score_stage(p, pl, q, k, v, beta, scores, score_row_stride, ws, (hipStream_t)stream);
 }
 
 int stem_quantize_score(const stem_problem* p, const void* q, const void* k, const void* v, void* q8, void* k8,

@@ -64,6 +64,7 @@ enum stem_status {
 enum stem_dtype { STEM_F32 = 0, STEM_BF16 = 1, STEM_FP8_E4M3 = 2 };
 
 #define STEM_MAX_REQS 256 /* requests per call */
+#define STEM_SCRATCH_BYTES (64u << 20) /* static scratch of stem_score_noalloc, per device */
 
 /* Problem descriptor shared by all entry points.  Read during the call only. */
 typedef struct stem_problem {
@@ -123,6 +124,19 @@ int stem_score(const stem_problem* p, const void* q, const void* k, const void* 
 int stem_tpd_topk(const stem_problem* p, const float* scores, int64_t score_row_stride, int32_t rho_num,
                   int32_t rho_den, int32_t mu_num, int32_t mu_den, uint32_t* mask, int32_t mask_row_words,
                   int32_t* counts, void* stream);
+
+/* Stage 1 without a workspace, for callers that cannot allocate device memory (code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid allocation).  Same arguments, kernels and
+ * results as stem_score, minus ws/ws_bytes: the pooled q-bar, k-bar and M go to a static scratch array
+ * the library holds in each device's memory (STEM_SCRATCH_BYTES, allocated when the library's code is
+ * loaded on the device and kept until the process ends; nothing is allocated by the call).  A problem
+ * whose workspace (stem_workspace_bytes) exceeds STEM_SCRATCH_BYTES is rejected with STEM_E_UNSUPPORTED
+ * before anything is enqueued; 64 MiB holds up to 3,271 blocks (418K tokens at block 128) of a layer with
+ * 32 query / 8 KV heads of head_dim 128.
+ * Every call on a device shares that device's scratch and leaves its pooled tensors there: calls that
+ * may overlap on one device (several streams or threads) race, so serialise them. */
+int stem_score_noalloc(const stem_problem* p, const void* q, const void* k, const void* v, float beta,
+                       float* scores, int64_t score_row_stride, void* stream);
 
 /* Stage 1 for an fp8 (W8A8) layer from bf16 activations: quantisation fused with pooling -------------- */
 /* q, k, v: DEVICE bf16 in the layouts above (contiguous K/V).  Writes the per-head scales

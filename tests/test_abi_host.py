@@ -198,6 +198,7 @@ def test_invalid_problem_is_rejected_by_every_entry_point(kw, msg):
         lambda: stem.block_counts(p),
         lambda: stem.workspace_layout(p),
         lambda: stem.stem_score(p, T(), T(), T(), 0.2, T(shape=(1, 1, 64)), T(shape=(1 << 30,), elem=1), stream=0),
+        lambda: stem.stem_score_noalloc(p, T(), T(), T(), 0.2, T(shape=(1, 1, 64)), stream=0),
         lambda: stem.stem_tpd_topk(p, T(shape=(1, 1, 64)), (1, 4), (7, 10), T(shape=(1, 1, 2)), T(), stream=0),
         lambda: stem.bsa_prefill(p, T(), T(), T(), None, T(), stream=0),
         lambda: _abi.bsa_prefill_inloop(p, T(), T(), T(), T(shape=(8, 24, 1)), T(), stream=0),
@@ -309,6 +310,34 @@ def test_score_select_argument_errors():
         stem.stem_score_select(big, T(), T(), T(), 0.2, (1, 4), (7, 10), T(shape=(8, nb, (mx + 31) // 32)), T(),
                                T(shape=(stem.workspace_bytes(big),), elem=1), stream=0)
     assert e.value.status == _abi.STEM_E_UNSUPPORTED
+
+
+def test_noalloc_scoring_validation_and_scratch_limit():
+    """stem_score_noalloc validates like stem_score and rejects, on the host, a problem whose pooled tensors
+    exceed the static scratch (STEM_SCRATCH_BYTES in the header)."""
+    T = _FakeTensor
+    src = open(HEADER).read()
+    m = re.search(r"#define STEM_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == _abi.SCRATCH_BYTES
+    p = _prob()  # NB = 24, max_n = 16
+    for call, msg in [
+        (lambda: stem.stem_score_noalloc(p, T(), T(), T(), 0.2, T(shape=(8, 24, 15)), stream=0), "score_row_stride"),
+        (lambda: stem.stem_score_noalloc(p, T(), T(), T(), float("nan"), T(shape=(8, 24, 16)), stream=0), "beta"),
+        (lambda: stem.stem_score_noalloc(p, T(addr=0x10008), T(), T(), 0.2, T(shape=(8, 24, 16)), stream=0),
+         "aligned"),
+        (lambda: stem.stem_score_noalloc(p, None, T(), T(), 0.2, T(shape=(8, 24, 16)), stream=0), "non-NULL"),
+    ]:
+        with pytest.raises(stem.StemError) as e:
+            call()
+        assert msg in str(e.value), str(e.value)
+    # 32 query / 8 KV heads, head_dim 128: 3271 blocks fit in 64 MiB, 3272 do not
+    for nb, fits in ((3271, True), (3272, False)):
+        q = _prob(cu_seqlens=[0, nb * 128], hq=32, hkv=8, head_dim=128, block=128)
+        assert (stem.workspace_bytes(q) <= _abi.SCRATCH_BYTES) == fits
+    big = _prob(cu_seqlens=[0, 3272 * 128], hq=32, hkv=8, head_dim=128, block=128)
+    with pytest.raises(stem.StemError) as e:
+        stem.stem_score_noalloc(big, T(), T(), T(), 0.2, T(shape=(32, 3272, 3272)), stream=0)
+    assert e.value.status == _abi.STEM_E_UNSUPPORTED and "static scratch" in str(e.value)
 
 
 def test_last_error_is_cleared_by_a_successful_call():
