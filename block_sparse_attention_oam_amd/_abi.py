@@ -28,7 +28,7 @@ SCRATCH_BYTES = 64 << 20  # STEM_SCRATCH_BYTES
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
            "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
            "bsa_prefill_inloop", "stem_score_select", "stem_naive_workspace_bytes", "stem_naive_score",
-           "stem_quantize_score", "stem_score_noalloc"]
+           "stem_quantize_score", "stem_score_noalloc", "stem_quantize_fp8"]
 
 
 class StemError(RuntimeError):
@@ -86,12 +86,13 @@ def lib() -> ctypes.CDLL:
         L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.stem_score_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
         L.stem_quantize_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, i64, vp, sz, vp]
+        L.stem_quantize_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.stem_naive_workspace_bytes.argtypes = [P, i32]
         L.stem_naive_workspace_bytes.restype = sz
         L.stem_naive_score.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, vp, i64, vp, sz, vp, sz, vp]
         for name in ("stem_block_counts", "stem_workspace_layout", "stem_tpd_budgets_host", "stem_score",
                      "stem_tpd_topk", "bsa_prefill", "bsa_prefill_inloop", "stem_score_select", "stem_naive_score", "stem_quantize_score",
-                     "stem_score_noalloc"):
+                     "stem_score_noalloc", "stem_quantize_fp8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -219,6 +220,12 @@ def stem_quantize_score(p: Problem, q, k, v, q8, k8, v8, q_scale, k_scale, v_sca
                                      _ptr(k_scale), _ptr(v_scale), float(beta), _ptr(scores),
                                      int(scores.shape[-1]) if scores is not None else 0, _ptr(ws),
                                      int(ws.numel() * ws.element_size()) if ws is not None else 0, _stream(stream)))
+
+
+def stem_quantize_fp8(p: Problem, q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, stream=None) -> None:
+    """bf16 q, k, v -> e4m3fn codes and per-head scales (no pooling)."""
+    _check(lib().stem_quantize_fp8(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+                                   _ptr(k_scale), _ptr(v_scale), _stream(stream)))
 
 
 def naive_workspace_bytes(p: Problem, samples: int) -> int:

@@ -279,6 +279,19 @@ __global__ void zero_kernel(float* s, int n) {
   if (i < n) s[i] = 0.f;
 }
 
+// W8A8 quantisation alone: bf16 x [tokens][H][d] -> e4m3fn codes with the per-head scales already in
+// `scale`; each thread converts 16 consecutive elements of one head (32 bytes in, 16 bytes out) with the
+// same arithmetic as the quantising pool.  HBM-bound streaming.
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t* x, uint8_t* codes, const float* scale, int H,
+                                                    int d, int64_t n16) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n16) return;
+  const int64_t e0 = idx * 16;
+  const int head = (int)((e0 / d) % H);
+  const uint4* src = (const uint4*)(x + e0);
+  *(uint4*)(codes + e0) = quant16(src[0], src[1], scale[head]);
+}
+
 constexpr int kTile = 64;
 constexpr int kDChunk = 32;
 
@@ -357,8 +370,9 @@ hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quant_pool(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
-                             hipStream_t s) {
+// Per-head scales of bf16 Q, K, V: amax over all tokens, then amax / 448 (1 for an all-zero head).
+static void launch_scales(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
+                          hipStream_t s) {
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((a.hq + 255) / 256)), dim3(256), 0, s, q_scale, a.hq);
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, k_scale, a.hkv);
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, v_scale, a.hkv);
@@ -367,6 +381,24 @@ hipError_t launch_quant_pool(const PoolArgs& a, float* q_scale, float* k_scale, 
   hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((a.hq + 255) / 256)), dim3(256), 0, s, q_scale, a.hq);
   hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, k_scale, a.hkv);
   hipLaunchKernelGGL(scale_kernel, dim3((unsigned)((a.hkv + 255) / 256)), dim3(256), 0, s, v_scale, a.hkv);
+}
+
+hipError_t launch_quant(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
+                        hipStream_t s) {
+  launch_scales(a, q_scale, k_scale, v_scale, tokens, s);
+  const int64_t nq = tokens * a.hq * a.d / 16, nkv = tokens * a.hkv * a.d / 16;
+  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, (const uint16_t*)a.q,
+                     (uint8_t*)a.q8, (const float*)q_scale, a.hq, a.d, nq);
+  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)((nkv + 255) / 256)), dim3(256), 0, s, (const uint16_t*)a.k,
+                     (uint8_t*)a.k8, (const float*)k_scale, a.hkv, a.d, nkv);
+  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)((nkv + 255) / 256)), dim3(256), 0, s, (const uint16_t*)a.v,
+                     (uint8_t*)a.v8, (const float*)v_scale, a.hkv, a.d, nkv);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pool(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
+                             hipStream_t s) {
+  launch_scales(a, q_scale, k_scale, v_scale, tokens, s);
   PoolArgs b = a;
   b.q_scale = q_scale;
   b.k_scale = k_scale;

@@ -352,6 +352,36 @@ int stem_score_noalloc(const stem_problem* p, const void* q, const void* k, cons
   return launch_score_stage(p, pl, q, k, v, beta, scores, score_row_stride, ws, (hipStream_t)stream);
 }
 
+int stem_quantize_fp8(const stem_problem* p, const void* q, const void* k, const void* v, void* q8, void* k8,
+                      void* v8, float* q_scale, float* k_scale, float* v_scale, void* stream) {
+  Plan pl;
+  int st = make_plan(p, &pl);
+  if (st != STEM_OK) return st;
+  if (p->dtype != STEM_FP8_E4M3 || p->kv_paged)
+    return fail(STEM_E_UNSUPPORTED, "quantisation describes an fp8 layer with contiguous K/V");
+  if (!q || !k || !v || !q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale)
+    return fail(STEM_E_INVALID_ARG, "q, k, v, q8, k8, v8 and the scale arrays must be non-NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)q8 | (uintptr_t)k8 | (uintptr_t)v8) & 15)
+    return fail(STEM_E_INVALID_ARG, "q, k, v, q8, k8 and v8 must be 16-byte aligned");
+  st = check_device();
+  if (st != STEM_OK) return st;
+  PoolArgs pa;
+  pa.q = q;
+  pa.k = k;
+  pa.v = v;
+  pa.q8 = q8;
+  pa.k8 = k8;
+  pa.v8 = v8;
+  pa.hq = p->hq;
+  pa.hkv = p->hkv;
+  pa.d = p->head_dim;
+  pa.B = p->block;
+  pa.NB = pl.NB;
+  pa.kv = pl.kv;
+  pa.rt = pl.rt;
+  return hip_status(launch_quant(pa, q_scale, k_scale, v_scale, pl.tokens, (hipStream_t)stream), "quantise launch");
+}
+
 int stem_quantize_score(const stem_problem* p, const void* q, const void* k, const void* v, void* q8, void* k8,
                         void* v8, float* q_scale, float* k_scale, float* v_scale, float beta, float* scores,
                         int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream) {

@@ -115,6 +115,9 @@ hipError_t launch_pool(const PoolArgs& a, int dtype, hipStream_t s);
 // bf16 inputs -> per-head amax into the scale arrays, scales, then the quantising pool (fp8 codes out).
 hipError_t launch_quant_pool(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
                              hipStream_t s);
+// bf16 inputs -> per-head scales and e4m3fn codes, no pooling.
+hipError_t launch_quant(const PoolArgs& a, float* q_scale, float* k_scale, float* v_scale, int64_t tokens,
+                        hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int max_n, int num_reqs, hipStream_t s);
 hipError_t launch_score_topk(const ScoreTopkArgs& a, int max_n, int num_reqs, hipStream_t s);

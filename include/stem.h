@@ -152,6 +152,14 @@ int stem_quantize_score(const stem_problem* p, const void* q, const void* k, con
                         void* v8, float* q_scale, float* k_scale, float* v_scale, float beta, float* scores,
                         int64_t score_row_stride, void* ws, size_t ws_bytes, void* stream);
 
+/* W8A8 quantisation alone: the first half of stem_quantize_score without the pooling.  Same inputs,
+ * scales and codes (bit for bit); reads the bf16 inputs twice (per-head amax, then the codes) and writes
+ * the codes once.  stem_score on its outputs then gives what stem_quantize_score gives.  It exists as the
+ * unfused baseline of that fusion, and for callers that quantise without scoring.
+ * Source: "答案不在算法里" (W8A8-FP8 deployment). */
+int stem_quantize_fp8(const stem_problem* p, const void* q, const void* k, const void* v, void* q8, void* k8,
+                      void* v8, float* q_scale, float* k_scale, float* v_scale, void* stream);
+
 /* Stages 1 + 2 fused: the score tensor never reaches memory ---------------------------------------- */
 /* Pools Q/K/V into the workspace exactly as stem_score does, then computes each row's block scores on
  * chip and selects from them exactly as stem_tpd_topk does: mask and counts are bit-identical to

@@ -340,6 +340,31 @@ def test_noalloc_scoring_validation_and_scratch_limit():
     assert e.value.status == _abi.STEM_E_UNSUPPORTED and "static scratch" in str(e.value)
 
 
+def test_quantize_fp8_argument_errors():
+    """The quantise-only entry point describes an fp8 layer with contiguous K/V and needs every buffer."""
+    T = _FakeTensor
+    f8 = dict(dtype="fp8", q_scale=T(), k_scale=T(), v_scale=T())
+    p = _prob(**f8)
+    args = [T() for _ in range(9)]
+    with pytest.raises(stem.StemError) as e:
+        stem.stem_quantize_fp8(_prob(), *args, stream=0)
+    assert e.value.status == _abi.STEM_E_UNSUPPORTED
+    with pytest.raises(stem.StemError) as e:
+        stem.stem_quantize_fp8(_prob(page_table=T(shape=(2, 64)), page_size=64, num_pages=40, **f8), *args, stream=0)
+    assert e.value.status == _abi.STEM_E_UNSUPPORTED
+    for bad, msg in ((3, "non-NULL"), (7, "non-NULL")):
+        a = list(args)
+        a[bad] = None
+        with pytest.raises(stem.StemError) as e:
+            stem.stem_quantize_fp8(p, *a, stream=0)
+        assert msg in str(e.value)
+    a = list(args)
+    a[4] = T(addr=0x10008)
+    with pytest.raises(stem.StemError) as e:
+        stem.stem_quantize_fp8(p, *a, stream=0)
+    assert "aligned" in str(e.value)
+
+
 def test_last_error_is_cleared_by_a_successful_call():
     with pytest.raises(stem.StemError):
         stem.block_counts(_prob(hq=3, hkv=2))

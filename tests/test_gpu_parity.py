@@ -466,6 +466,40 @@ def test_quantize_score_codes_scales_and_pooling(dev, over):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("over", [dict(lens=(1000,), hq=8, hkv=2), dict(lens=(200, 513), hq=4, hkv=1, d=64)])
+def test_quantize_fp8_alone_matches_oracle_and_fused_stage(dev, over):
+    """stem_quantize_fp8 (no pooling): scales and codes bit-exact against the oracle's quantisation and
+    equal to stem_quantize_score's; stem_score on them gives stem_quantize_score's scores."""
+    import block_sparse_attention_oam_amd as stem
+    from block_sparse_attention_oam_amd.layer import StemPrefill, upload
+
+    pb = synth.make_problem("w8a8_128k_fp8", dtype="bf16", **over)
+    p8 = synth.make_problem("w8a8_128k_fp8", **over)
+    xb = synth.make_inputs(pb, seed=5)
+    L1, _, codes, scales = _quantize_and_reference(p8, xb, dev)
+    q, k, v = upload(xb["q"]), upload(xb["k"]), upload(xb["v"])
+    c2 = [torch.full(t.shape, 0xAB, dtype=torch.uint8, device=dev) for t in (q, k, v)]
+    s2 = [torch.full((n,), float("nan"), dtype=torch.float32, device=dev) for n in (p8.hq, p8.hkv, p8.hkv)]
+    prob = stem.make_problem(p8.cu_seqlens, p8.hq, p8.hkv, p8.d, p8.block, "fp8", q_scale=s2[0], k_scale=s2[1],
+                             v_scale=s2[2])
+    stem.stem_quantize_fp8(prob, q, k, v, *c2, *s2)
+    L3 = StemPrefill(prob, dev)
+    L3.scores.fill_(float("nan"))
+    L3.score(*c2, p8.beta)
+    torch.cuda.synchronize()
+    for name, c, s_, cf, sf in zip("qkv", c2, s2, codes, scales):
+        want_c, want_s = oracle.quantize_fp8_per_head(oracle.bf16_to_f64(xb[name]))
+        assert np.array_equal(s_.cpu().numpy(), want_s), name
+        assert np.array_equal(c.cpu().numpy(), want_c), name
+        assert torch.equal(c, cf) and torch.equal(s_, sf), name
+    for r in range(len(p8.lens)):
+        nr = p8.nblocks(r)
+        tri = torch.tril(torch.ones(nr, nr, dtype=torch.bool, device=dev))
+        a = L1.scores[:, p8.cu_blocks[r]:p8.cu_blocks[r + 1], :nr][:, tri]
+        b = L3.scores[:, p8.cu_blocks[r]:p8.cu_blocks[r + 1], :nr][:, tri]
+        assert torch.equal(a, b)
+
+
 @pytest.mark.timeout(600)
 def test_quantize_score_full_size_128k(dev):
     """The 128K fp8 layer from its bf16 activations: scales bit-exact, codes bit-exact on sampled token
