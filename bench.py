@@ -96,6 +96,50 @@ def time_layer(L, q, k, v, p, steps, warmup, torch):
     return wall, stage.mean(axis=0), stage[:, 2]
 
 
+def time_layer_cold(L, q, k, v, p, steps, warmup, torch, dev):
+    """The headline protocol: `warmup` untimed steps, then `steps` steps each preceded by overwriting a 1 GiB
+    buffer (evicts L2 and the 256 MB MALL; outside the step's events).  Returns the median layer time, the
+    per-stage medians, every step's BSA time, and the wall time per step (flush included)."""
+    rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        L.forward(q, k, v, p.beta, rho, mu)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        scratch.fill_(1)
+        e = evs[s]
+        e[0].record()
+        L.score(q, k, v, p.beta)
+        e[1].record()
+        L.select(rho, mu)
+        e[2].record()
+        L.attend(q, k, v, "selected", True)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs])  # ms
+    layer = stage.sum(axis=1)
+    del scratch
+    return float(np.median(layer)), np.median(stage, axis=0), stage[:, 2], layer, wall
+
+
+def stage_bytes(p):
+    """Algorithmic HBM bytes of the two selection stages.  Scoring: one read of Q, K and V, the pooled
+    q-bar, k-bar, M written once, the causal block scores written once.  Selection: the causal scores read
+    once, the mask and the counts written once."""
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[p.dtype]
+    nb = [p.nblocks(r) for r in range(len(p.lens))]
+    NB = sum(nb)
+    words = (max(nb) + 31) // 32
+    causal = sum(n * (n + 1) // 2 for n in nb)
+    inputs = p.tokens * (p.hq + 2 * p.hkv) * p.d * eb
+    pooled = ((p.hq + p.hkv) * p.d + p.hkv) * NB * 4
+    scores = p.hq * causal * 4
+    return inputs + pooled + scores, scores + p.hq * NB * (words + 1) * 4
+
+
 def time_bsa(L, q, k, v, mask, reps, torch, inloop=False):
     L.attend(q, k, v, mask, False, inloop=inloop)
     torch.cuda.synchronize()
@@ -115,7 +159,7 @@ def measure_other(name, steps, warmup, dev, torch):
     p = synth.make_problem(name)
     x = synth.make_inputs(p, seed=0)
     L, q, k, v = setup(p, x, dev)
-    ms, stage, bsa_each = time_layer(L, q, k, v, p, steps, warmup, torch)
+    ms, stage, bsa_each, _, _ = time_layer_cold(L, q, k, v, p, steps, warmup, torch, dev)
     fl = 4 * p.d * visible_pairs(p, L.mask.cpu().numpy().view(np.uint32), L.NB)
     bsa = float(np.mean(bsa_each))
     peak = PEAK[p.dtype]
@@ -261,33 +305,19 @@ def measure_quantize(dev, torch, reps):
 
     t_fused = run(lambda: stem.stem_quantize_score(prob, q, k, v, q8, k8, v8, qs, ks, vs, pb.beta, L.scores, L.ws))
     t_score = run(lambda: L.score(q8, k8, v8, pb.beta))
+    t_quant = run(lambda: stem.stem_quantize_fp8(prob, q, k, v, q8, k8, v8, qs, ks, vs))
+
+    def unfused():
+        stem.stem_quantize_fp8(prob, q, k, v, q8, k8, v8, qs, ks, vs)
+        L.score(q8, k8, v8, pb.beta)
+
+    t_unfused = run(unfused)
     bf16_bytes = int(sum(t.numel() * 2 for t in (q, k, v)))
     return {"workload": "w8a8_128k_fp8 from bf16 activations", "quantize_score_ms": round(t_fused, 4),
-            "score_on_fp8_ms": round(t_score, 4), "bf16_bytes_read_twice": bf16_bytes,
-            "fp8_bytes_written": bf16_bytes // 2,
-            "note": "a separate quantiser would read bf16 twice and write fp8, then stem_score reads the fp8 again"}
-
-
-def measure_cold(L, q, k, v, p, torch, dev, steps=20, warmup=5):
-    """Layer time with the caches evicted before every step (a 1 GiB buffer is overwritten between
-    steps, outside the timed events): median, p10 and p90 over the steps, after `warmup` untimed ones."""
-    rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        L.forward(q, k, v, p.beta, rho, mu)
-    times = []
-    for _ in range(steps):
-        scratch.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        L.forward(q, k, v, p.beta, rho, mu)
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    del scratch
-    t = np.array(times)
-    return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
-            "p90": round(float(np.percentile(t, 90)), 4), "steps": steps, "warmup": warmup}
+            "unfused_quantize_then_score_ms": round(t_unfused, 4), "quantize_only_ms": round(t_quant, 4),
+            "score_on_fp8_ms": round(t_score, 4), "fusion_speedup": round(t_unfused / t_fused, 3),
+            "bf16_bytes_read_twice": bf16_bytes, "fp8_bytes_written": bf16_bytes // 2,
+            "note": "unfused: stem_quantize_fp8 (amax pass, then codes) followed by stem_score on the codes"}
 
 
 def host_cpu():
@@ -402,8 +432,12 @@ def main():
     log(f"[bench] generating {describe(p)}")
     x = synth.make_inputs(p, seed=0)
     L, q, k, v = setup(p, x, dev)
-    log("[bench] timing the layer")
-    ms_step, stage_ms, bsa_each = time_layer(L, q, k, v, p, args.steps, args.warmup, torch)
+    log("[bench] timing the layer (cold: 1 GiB overwritten before each step)")
+    ms_step, stage_ms, bsa_each, layer_each, wall_step = time_layer_cold(L, q, k, v, p, args.steps, args.warmup,
+                                                                         torch, dev)
+    log("[bench] warm steps (no eviction)")
+    _, warm_stage, _ = time_layer(L, q, k, v, p, args.steps, 1, torch)
+    warm_ms = float(np.sum(warm_stage))
     words = L.mask.cpu().numpy().view(np.uint32)
     pairs = visible_pairs(p, words, L.NB)
     flops = 4 * p.d * pairs
@@ -427,11 +461,23 @@ def main():
         "data": "synthetic (seeded; Llama-3-8B-shaped layer, no weights or datasets)",
         "config": {"workload": describe(p), "tokens": p.tokens, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * tflops / peak, 2),
+        "timing": ("ms_per_step = median over the timed steps of the layer's HIP-event time, each step after "
+                   "a 1 GiB buffer was overwritten (cold L2 and MALL); warm = the same steps back to back"),
+        "ms_per_step_p10_p90": [round(float(np.percentile(layer_each, 10)), 4),
+                                round(float(np.percentile(layer_each, 90)), 4)],
+        "wall_ms_per_step_with_eviction": round(wall_step, 4),
+        "warm": {"ms_per_step": round(warm_ms, 4), "tflops": round(flops / (warm_ms * 1e-3) / 1e12, 2),
+                 "stages_ms": [round(float(t), 4) for t in warm_stage]},
         "stages_ms": {"stem_score": round(float(stage_ms[0]), 4), "stem_tpd_topk": round(float(stage_ms[1]), 4),
                       "bsa_prefill": round(float(stage_ms[2]), 4)},
         "selected_density": round(density, 5),
         "effective_flop_per_layer": flops,
     }
+    sb, selb = stage_bytes(p)
+    out["scoring_hbm"] = {"algorithmic_bytes": sb, "gbps": round(sb / (stage_ms[0] * 1e-3) / 1e9, 1),
+                          "frac_of_8TBps": round(sb / (stage_ms[0] * 1e-3) / 8e12, 4)}
+    out["selection_hbm"] = {"algorithmic_bytes": selb, "gbps": round(selb / (stage_ms[1] * 1e-3) / 1e9, 1),
+                            "frac_of_8TBps": round(selb / (stage_ms[1] * 1e-3) / 8e12, 4)}
     # Roofline of the dominant kernel (block-sparse attention): effective flops / average launch time.
     kernel_src = {"bf16": "bsa_bf16.hip", "fp8": "bsa_fp8.hip"}.get(p.dtype, "bsa_fwd.hip")
     src = open(os.path.join(ROOT, "block_sparse_attention_oam_amd", "csrc", kernel_src), "rb").read()
@@ -440,8 +486,6 @@ def main():
                        "unit": "TFLOP/s", "frac": round(bsa_tflops / peak, 4),
                        "traffic": traffic_from_profile(sha), "avg_launch_ms": round(bsa_ms, 4)}
     if not args.no_extras:
-        log("[bench] cold steps (1 GiB written between steps to evict L2 and MALL)")
-        out["cold_layer_ms"] = measure_cold(L, q, k, v, p, torch, dev)
         log("[bench] fused scoring + selection")
         rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
         ref_mask = L.mask.clone()
@@ -455,8 +499,8 @@ def main():
         torch.cuda.synchronize()
         fused_ms = ev[0].elapsed_time(ev[1]) / 5
         out["fused_score_select"] = {
-            "ms": round(fused_ms, 4), "two_stage_ms": round(float(stage_ms[0] + stage_ms[1]), 4),
-            "speedup": round(float(stage_ms[0] + stage_ms[1]) / fused_ms, 3),
+            "ms": round(fused_ms, 4), "two_stage_ms": round(float(warm_stage[0] + warm_stage[1]), 4),
+            "speedup": round(float(warm_stage[0] + warm_stage[1]) / fused_ms, 3),
             "same_mask": bool(torch.equal(ref_mask, L.mask)),
             "score_tensor_bytes_avoided": int(4 * sum(p.hq * p.nblocks(r) * (p.nblocks(r) + 1) for r in range(len(p.lens)))),
         }
