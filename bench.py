@@ -387,9 +387,12 @@ def cpu_baseline(p, x, tokens=65536):
     return 4 * p.d * vis / dt / 1e12, threads, desc, {k_: round(v_, 3) for k_, v_ in st.items()}
 
 
-def traffic_from_profile(src_sha):
+def traffic_from_profile(src_sha, kernel_src="bsa_bf16.hip"):
     """HBM bytes per BSA launch from the committed PMC summary, if it was taken on the current kernel."""
-    path = os.path.join(ROOT, "profiles", "bsa_traffic.json")
+    name = {"bsa_bf16.hip": "bsa_traffic.json", "bsa_fp8.hip": "bsa_fp8_traffic.json"}.get(kernel_src)
+    if name is None:
+        return None
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
@@ -484,7 +487,7 @@ def main():
     sha = hashlib.sha256(src).hexdigest()
     out["roofline"] = {"kernel": kernel_src.replace(".hip", "_kernel"), "bound": "mfma", "achieved": round(bsa_tflops, 2), "peak": peak,
                        "unit": "TFLOP/s", "frac": round(bsa_tflops / peak, 4),
-                       "traffic": traffic_from_profile(sha), "avg_launch_ms": round(bsa_ms, 4)}
+                       "traffic": traffic_from_profile(sha, kernel_src), "avg_launch_ms": round(bsa_ms, 4)}
     if not args.no_extras:
         log("[bench] fused scoring + selection")
         rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
