@@ -152,6 +152,35 @@ def time_bsa(L, q, k, v, mask, reps, torch, inloop=False):
     return a.elapsed_time(b) / reps
 
 
+def fused_vs_two_stage(L, q, k, v, p, torch, reps=10):
+    """Fused scoring + selection (stem_score_select) against the two stages run back to back, both warm,
+    each timed over `reps` calls; the fused masks are checked against the two-stage ones."""
+    rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
+    L.score(q, k, v, p.beta)
+    L.select(rho, mu)
+    torch.cuda.synchronize()
+    ref_mask, ref_counts = L.mask.clone(), L.counts.clone()
+
+    def run(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    two = run(lambda: (L.score(q, k, v, p.beta), L.select(rho, mu)))
+    L.mask.zero_()
+    fused = run(lambda: L.score_select(q, k, v, p.beta, rho, mu))
+    return {"ms": round(fused, 4), "two_stage_ms": round(two, 4), "speedup": round(two / fused, 3),
+            "same_mask": bool(torch.equal(ref_mask, L.mask) and torch.equal(ref_counts, L.counts)),
+            "score_tensor_bytes_avoided": int(4 * sum(p.hq * p.nblocks(r) * (p.nblocks(r) + 1)
+                                                      for r in range(len(p.lens))))}
+
+
 def measure_other(name, steps, warmup, dev, torch):
     """ms/layer and effective TFLOP/s of another workload (same step: score, select, attend)."""
     import synth
@@ -163,10 +192,13 @@ def measure_other(name, steps, warmup, dev, torch):
     fl = 4 * p.d * visible_pairs(p, L.mask.cpu().numpy().view(np.uint32), L.NB)
     bsa = float(np.mean(bsa_each))
     peak = PEAK[p.dtype]
-    return {"workload": describe(p), "dtype": p.dtype, "ms_per_layer": round(ms, 4),
-            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "pct_of_peak": round(100 * fl / (ms * 1e-3) / 1e12 / peak, 2),
-            "stages_ms": [round(float(t), 4) for t in stage], "bsa_tflops": round(fl / (bsa * 1e-3) / 1e12, 2),
-            "peak_tflops": peak}
+    out = {"workload": describe(p), "dtype": p.dtype, "ms_per_layer": round(ms, 4),
+           "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "pct_of_peak": round(100 * fl / (ms * 1e-3) / 1e12 / peak, 2),
+           "stages_ms": [round(float(t), 4) for t in stage], "bsa_tflops": round(fl / (bsa * 1e-3) / 1e12, 2),
+           "peak_tflops": peak}
+    if max(p.nblocks(r) for r in range(len(p.lens))) <= 2048:
+        out["fused_score_select"] = fused_vs_two_stage(L, q, k, v, p, torch)
+    return out
 
 
 def unpack_bits(p, words, r, NB_off):
@@ -490,23 +522,8 @@ def main():
                        "traffic": traffic_from_profile(sha, kernel_src), "avg_launch_ms": round(bsa_ms, 4)}
     if not args.no_extras:
         log("[bench] fused scoring + selection")
-        rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
-        ref_mask = L.mask.clone()
-        L.score_select(q, k, v, p.beta, rho, mu)
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record()
-        for _ in range(5):
-            L.score_select(q, k, v, p.beta, rho, mu)
-        ev[1].record()
-        torch.cuda.synchronize()
-        fused_ms = ev[0].elapsed_time(ev[1]) / 5
-        out["fused_score_select"] = {
-            "ms": round(fused_ms, 4), "two_stage_ms": round(float(warm_stage[0] + warm_stage[1]), 4),
-            "speedup": round(float(warm_stage[0] + warm_stage[1]) / fused_ms, 3),
-            "same_mask": bool(torch.equal(ref_mask, L.mask)),
-            "score_tensor_bytes_avoided": int(4 * sum(p.hq * p.nblocks(r) * (p.nblocks(r) + 1) for r in range(len(p.lens)))),
-        }
+        out["fused_score_select"] = fused_vs_two_stage(L, q, k, v, p, torch)
+        fused_ms = out["fused_score_select"]["ms"]
         if p.dtype == "bf16" and not p.paged:
             log("[bench] naive token-level scoring (comparison path)")
             out["naive_scoring"] = measure_naive(L, q, k, v, p, dev, torch, float(stage_ms[0]), fused_ms)
