@@ -23,7 +23,7 @@ SOURCES = ["stem_api.hip", "pool_score.hip", "tpd_topk.hip", "score_topk.hip", "
 # Packed-fp32 VALU ops are disabled for all device code; the host pass warns that it does not know the
 # feature, which is harmless.
 HIPFLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]

@@ -92,8 +92,13 @@ __device__ __forceinline__ typename RawChunk<EB>::type zero_chunk() {
   else return make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Two workgroups per CU are asked of the register allocator only where they fit (d = 64, 16-bit K/V);
+// the other instances need more registers than that allows.
+template <int D, int EB>
+constexpr int kMinBlocks = (D == 64 && EB != 4) ? 2 : 1;
+
 template <int D, int EB, int NW, bool MASKED>
-__global__ __launch_bounds__(NW * 64, 2) void bsa_kernel(BsaArgs a) {
+__global__ __launch_bounds__(NW * 64, (kMinBlocks<D, EB>)) void bsa_kernel(BsaArgs a) {
   using C = Cfg<D, EB>;
   using lds_t = typename C::lds_t;
   using raw_t = typename RawChunk<EB>::type;

@@ -32,8 +32,6 @@ int ok() {
   return STEM_OK;
 }
 
-constexpr int64_t kMaxTokens = (int64_t)1 << 31;
-
 // Validate the descriptor and derive the plan (request tables, block counts).  Pure host code.
 int make_plan(const stem_problem* p, Plan* plan) {
   if (!p) return fail(STEM_E_INVALID_ARG, "problem descriptor is NULL");
@@ -59,7 +57,6 @@ int make_plan(const stem_problem* p, Plan* plan) {
   for (int r = 0; r < p->num_reqs; ++r) {
     const int64_t len = (int64_t)p->cu_seqlens[r + 1] - p->cu_seqlens[r];
     if (len < 0) return fail(STEM_E_INVALID_ARG, "cu_seqlens decreases at request %d", r);
-    if (p->cu_seqlens[r + 1] >= kMaxTokens) return fail(STEM_E_UNSUPPORTED, "more than 2^31 tokens");
     const int64_t n = (len + p->block - 1) / p->block;
     nb += n;
     if (n > max_n) max_n = (int32_t)n;
