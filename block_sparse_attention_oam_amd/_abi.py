@@ -13,7 +13,8 @@ from dataclasses import dataclass
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libstem.so")
+# STEM_LIB names another build of the same library (the host-sanitized one the CPU tests load).
+LIB_PATH = os.environ.get("STEM_LIB") or os.path.join(_PKG, "libstem.so")
 
 STEM_OK = 0
 STEM_E_INVALID_ARG = -1
