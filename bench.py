@@ -140,13 +140,13 @@ def stage_bytes(p):
     return inputs + pooled + scores, scores + p.hq * NB * (words + 1) * 4
 
 
-def time_bsa(L, q, k, v, mask, reps, torch, inloop=False):
-    L.attend(q, k, v, mask, False, inloop=inloop)
+def time_bsa(L, q, k, v, mask, reps, torch, inloop=False, expand_v=True):
+    L.attend(q, k, v, mask, False, inloop=inloop, expand_v=expand_v)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        L.attend(q, k, v, mask, False, inloop=inloop)
+        L.attend(q, k, v, mask, False, inloop=inloop, expand_v=expand_v)
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / reps
@@ -198,6 +198,13 @@ def measure_other(name, steps, warmup, dev, torch):
            "peak_tflops": peak}
     if max(p.nblocks(r) for r in range(len(p.lens))) <= 2048:
         out["fused_score_select"] = fused_vs_two_stage(L, q, k, v, p, torch)
+    if L.bsa_ws.numel() > 0:
+        # fp8: bsa_prefill_ws (V expanded to bf16 once per call, expansion included) against bsa_prefill
+        # (V converted on every tile visit), warm, same selection
+        t_ws = time_bsa(L, q, k, v, "selected", 3, torch)
+        t_pv = time_bsa(L, q, k, v, "selected", 3, torch, expand_v=False)
+        out["v_expansion"] = {"bsa_prefill_ws_ms": round(t_ws, 4), "bsa_prefill_per_visit_ms": round(t_pv, 4),
+                              "speedup": round(t_pv / t_ws, 3), "workspace_bytes": int(L.bsa_ws.numel())}
     return out
 
 

@@ -29,7 +29,7 @@ SCRATCH_BYTES = 64 << 20  # STEM_SCRATCH_BYTES
 EXPORTS = ["stem_block_counts", "stem_workspace_bytes", "stem_workspace_layout", "stem_tpd_budgets_host",
            "stem_status_string", "stem_last_error", "stem_score", "stem_tpd_topk", "bsa_prefill",
            "bsa_prefill_inloop", "stem_score_select", "stem_naive_workspace_bytes", "stem_naive_score",
-           "stem_quantize_score", "stem_score_noalloc", "stem_quantize_fp8"]
+           "stem_quantize_score", "stem_score_noalloc", "stem_quantize_fp8", "bsa_workspace_bytes", "bsa_prefill_ws"]
 
 
 class StemError(RuntimeError):
@@ -85,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.stem_tpd_topk.argtypes = [P, vp, i64, i32, i32, i32, i32, vp, i32, vp, vp]
         L.bsa_prefill.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
         L.bsa_prefill_inloop.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
+        L.bsa_workspace_bytes.argtypes = [P]
+        L.bsa_workspace_bytes.restype = sz
+        L.bsa_prefill_ws.argtypes = [P, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
         L.stem_score_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, i32, i32, i32, vp, i32, vp, vp, sz, vp]
         L.stem_quantize_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, i64, vp, sz, vp]
         L.stem_quantize_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -249,6 +252,21 @@ def bsa_prefill(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float =
     words = int(mask.shape[-1]) if mask is not None else 0
     _check(lib().bsa_prefill(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), words, float(softmax_scale),
                              _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def bsa_workspace_bytes(p: Problem) -> int:
+    """Workspace of bsa_prefill_ws (0 for problems that need none); raises on an invalid problem."""
+    block_counts(p)
+    return int(lib().bsa_workspace_bytes(p.ref))
+
+
+def bsa_prefill_ws(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float = 0.0, ws=None,
+                   stream=None) -> None:
+    """bsa_prefill with a workspace (fp8: V expanded to bf16 there first; same outputs)."""
+    words = int(mask.shape[-1]) if mask is not None else 0
+    nbytes = int(ws.numel() * ws.element_size()) if ws is not None else 0
+    _check(lib().bsa_prefill_ws(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(mask), words, float(softmax_scale),
+                                _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream)))
 
 
 def bsa_prefill_inloop(p: Problem, q, k, v, mask, out, lse=None, softmax_scale: float = 0.0, stream=None) -> None:

@@ -14,10 +14,14 @@
 //    the request's end read as zeros) into a swizzled tile (slot ^ ((row >> 1) & 7)); each lane reads its
 //    32-byte operand with two ds_read_b128.  Small pages look up one page per row.
 //  * O^T = V^T P^T stays on the bf16 matrix cores with P in bf16: rounding P to e4m3 (3 mantissa bits)
-//    misses the fp8 output tolerance on rows with few keys.  V is converted to bf16 once per sub-tile while
-//    it is staged (global -> registers -> v_cvt_scalef32_pk_bf16_fp8 -> LDS, each thread 1/(256 HEADS) of
-//    the tile, one sub-tile ahead), into the same swizzled bf16 tile the bf16 kernel reads with
-//    ds_read_b64_tr_b16.
+//    misses the fp8 output tolerance on rows with few keys.  V reaches LDS as bf16, in the same swizzled
+//    tile the bf16 kernel reads with ds_read_b64_tr_b16, in one of two ways:
+//      VB16 = false: the kernel converts each sub-tile of V codes while staging it (global -> registers ->
+//        v_cvt_scalef32_pk_bf16_fp8 -> LDS, each thread 1/(256 HEADS) of the tile, one sub-tile ahead);
+//      VB16 = true: V was expanded to bf16 once, before the launch (expand_fp8_kernel: exact, every e4m3
+//        value is a bf16 value), and sub-tiles go global -> LDS with buffer loads that write LDS, as K
+//        does: no conversion and no LDS store per visit.
+//    Both give the same bf16 tile, so the outputs are bit-identical.
 //  * softmax without a per-tile row max: the reference is set from a row's first visible keys and moves
 //    only when a tile's sum of P exceeds 2^32 (the tile is then recomputed from K, still in LDS); the row
 //    sum adds the rounded P pairs (v_dot2_f32_bf16).
@@ -68,10 +72,12 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 }
 
 // PAGE: 0 contiguous K/V, 1 pages of a multiple of 64 tokens (one page per sub-tile), 2 smaller pages.
-template <int PAGE, bool MASKED, int HEADS>
+// VB16: a.v holds V expanded to bf16 (same layout, 2-byte elements) instead of the e4m3 codes.
+template <int PAGE, bool MASKED, int HEADS, bool VB16>
 __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs a) {
   constexpr int NT = 256 * HEADS;
   constexpr int KPARTS = 2 / HEADS;    // 1 KB K loads per wave per sub-tile
+  constexpr int VPARTS = 4 / HEADS;    // 1 KB bf16 V loads per wave per sub-tile (VB16)
   constexpr int VCODES = KT * D / NT;  // V codes each thread stages per sub-tile (32 or 16)
   constexpr int VTPR = D / VCODES;     // threads per V row
   constexpr int VCH = VCODES / 8;      // 16-byte bf16 chunks each thread stores
@@ -225,6 +231,36 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
       }
     }
   };
+  // V expanded to bf16 (VB16): instruction m of this wave fills LDS chunk c = VPARTS*wave + m = tile rows
+  // 4c + lane/16 (256 bytes each), slot lane & 15, with the lane fetching source chunk slot ^ 4(row & 3):
+  // the swizzled tile that store_v writes in the other mode.
+  int vrow_ld[4], vchunk_ld[4], voff_ld[4];
+#pragma unroll
+  for (int m = 0; m < VPARTS; ++m) {
+    const int row = 4 * (VPARTS * wave + m) + (lane >> 4);
+    vrow_ld[m] = row;
+    vchunk_ld[m] = (lane & 15) ^ (4 * (row & 3));
+    voff_ld[m] = row * (int)(2 * row_stride) + vchunk_ld[m] * 16;
+  }
+  auto issue_v16 = [&](int u, uint8_t* vdst) {
+    const int kp0 = sub_key0(entry(u), u);
+    if (kp0 >= L) return;
+    lds_u8* vl = (lds_u8*)vdst + wave * (VPARTS * 1024);
+    if (PAGE == 0 || PAGE == 1) {
+      const int nrec = min(L - kp0, KT) * (int)(2 * row_stride);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase_all + 2 * key_row_off(kp0)), 0, nrec, kBufDword3);
+#pragma unroll
+      for (int m = 0; m < VPARTS; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, vl + m * 1024, 16, voff_ld[m], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int m = 0; m < VPARTS; ++m)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vbase_all + 2 * key_row_off(min(kp0 + vrow_ld[m], L - 1)) + vchunk_ld[m] * 16),
+            vl + m * 1024, 16, 0, 0);
+    }
+  };
   // V: thread t loads VCODES codes of tile row t / VTPR (dims VCODES (t % VTPR) ..), converts them to bf16
   // and stores VCH 16-byte chunks c = VCH (t % VTPR) + j at slot c ^ 4(row & 3) of the bf16 tile (256-byte
   // rows), in the order (j + row) mod VCH so that one store instruction spreads over the bank groups.
@@ -279,7 +315,8 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
     __syncthreads();
     const bool more = u + 1 < nsub;
     if (more) {
-      load_v(u + 1);
+      if constexpr (VB16) issue_v16(u + 1, vnext);
+      else load_v(u + 1);
       issue_k(u + 1, knext);
     }
     const uint32_t e = entry(u);
@@ -394,13 +431,19 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
         }
       }
     }
-    if (more) store_v(vnext);
+    if constexpr (!VB16)
+      if (more) store_v(vnext);
   };
 
   if (nsub > 0) {
-    load_v(0);
-    issue_k(0, kbuf0);
-    store_v(vbuf0);
+    if constexpr (VB16) {
+      issue_v16(0, vbuf0);
+      issue_k(0, kbuf0);
+    } else {
+      load_v(0);
+      issue_k(0, kbuf0);
+      store_v(vbuf0);
+    }
   }
   for (int u = 0; u < nsub; u += 2) {
     step(u, kbuf0, vbuf0, kbuf1, vbuf1);
@@ -410,7 +453,7 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
   // ---- epilogue
   const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
   if (!qvalid) return;
-  const float inv = (l_tot > 0.f) ? v_scale / l_tot : 0.f;  // the V codes were unscaled
+  const float inv = (l_tot > 0.f) ? v_scale / l_tot : 0.f;  // V (codes or their bf16 values) is unscaled
   const int64_t ooff = ((int64_t)(tb + qpos) * a.hq + h) * D;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -426,30 +469,63 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
         (l_tot > 0.f) ? (m_run + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
-}  // namespace
-
-bool bsa_fp8_supported(int dtype, int head_dim, int block) {
-  return dtype == STEM_FP8_E4M3 && head_dim == D && block == B;
+// V codes -> bf16 (exact), 16 codes per thread.  n is a multiple of 16; src and dst are 16-byte aligned.
+__global__ __launch_bounds__(256) void expand_fp8_kernel(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                         int64_t n16) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n16) return;
+  const uint4 w = ((const uint4*)src)[t];
+  const uint32_t c[4] = {w.x, w.y, w.z, w.w};
+  uint4 out[2];
+  uint32_t* o = (uint32_t*)out;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    o[2 * x] = fp8x2_to_bf16x2<false>(c[x]);
+    o[2 * x + 1] = fp8x2_to_bf16x2<true>(c[x]);
+  }
+  ((uint4*)dst)[2 * t] = out[0];
+  ((uint4*)dst)[2 * t + 1] = out[1];
 }
 
-template <bool MASKED, int HEADS>
+template <bool MASKED, int HEADS, bool VB16>
 static hipError_t launch_fp8_heads(const BsaArgs& args, hipStream_t s) {
   BsaArgs a = args;
   const int64_t wgs = (int64_t)(a.hq / HEADS) * a.NB;
   a.xcd_remap = wgs % 8 == 0 ? 1 : 0;
   const dim3 grid((unsigned)wgs), block(256 * HEADS);
   const int page_mode = !a.kv.paged ? 0 : (a.kv.page_size % KT == 0 ? 1 : 2);
-  if (page_mode == 0) hipLaunchKernelGGL((bsa_fp8_kernel<0, MASKED, HEADS>), grid, block, 0, s, a);
-  else if (page_mode == 1) hipLaunchKernelGGL((bsa_fp8_kernel<1, MASKED, HEADS>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((bsa_fp8_kernel<2, MASKED, HEADS>), grid, block, 0, s, a);
+  if (page_mode == 0) hipLaunchKernelGGL((bsa_fp8_kernel<0, MASKED, HEADS, VB16>), grid, block, 0, s, a);
+  else if (page_mode == 1) hipLaunchKernelGGL((bsa_fp8_kernel<1, MASKED, HEADS, VB16>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((bsa_fp8_kernel<2, MASKED, HEADS, VB16>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-// Two heads per workgroup whenever a KV group has an even number of query heads.
-hipError_t launch_bsa_fp8(const BsaArgs& a, bool masked, hipStream_t s) {
+template <bool VB16>
+static hipError_t launch_fp8_v(const BsaArgs& a, bool masked, hipStream_t s) {
   const bool pair = (a.hq / a.hkv) % 2 == 0;
-  if (masked) return pair ? launch_fp8_heads<true, 2>(a, s) : launch_fp8_heads<true, 1>(a, s);
-  return pair ? launch_fp8_heads<false, 2>(a, s) : launch_fp8_heads<false, 1>(a, s);
+  if (masked) return pair ? launch_fp8_heads<true, 2, VB16>(a, s) : launch_fp8_heads<true, 1, VB16>(a, s);
+  return pair ? launch_fp8_heads<false, 2, VB16>(a, s) : launch_fp8_heads<false, 1, VB16>(a, s);
+}
+
+}  // namespace
+
+bool bsa_fp8_supported(int dtype, int head_dim, int block) {
+  return dtype == STEM_FP8_E4M3 && head_dim == D && block == B;
+}
+
+// Two heads per workgroup whenever a KV group has an even number of query heads.
+hipError_t launch_bsa_fp8(const BsaArgs& a, bool masked, hipStream_t s) { return launch_fp8_v<false>(a, masked, s); }
+
+hipError_t launch_expand_fp8(const void* v_codes, void* v_bf16, int64_t n, hipStream_t s) {
+  const int64_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(expand_fp8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     (const uint8_t*)v_codes, (uint16_t*)v_bf16, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_bsa_fp8_vb16(const BsaArgs& a, bool masked, hipStream_t s) {
+  return launch_fp8_v<true>(a, masked, s);
 }
 
 }  // namespace stem

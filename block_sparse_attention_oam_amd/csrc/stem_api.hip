@@ -658,6 +658,46 @@ int bsa_prefill(const stem_problem* p, const void* q, const void* k, const void*
                     "bsa launch");
 }
 
+// V elements of the problem: every row of the contiguous tensor, or of the paged pool.
+static int64_t v_elements(const stem_problem* p, const Plan& pl) {
+  const int64_t rows = p->kv_paged ? (int64_t)p->num_pages * p->page_size : pl.tokens;
+  return rows * p->hkv * p->head_dim;
+}
+
+size_t bsa_workspace_bytes(const stem_problem* p) {
+  Plan pl;
+  if (make_plan(p, &pl) != STEM_OK) return 0;
+  ok();
+  if (!bsa_fp8_supported(p->dtype, p->head_dim, p->block)) return 0;
+  return (size_t)v_elements(p, pl) * 2;
+}
+
+int bsa_prefill_ws(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
+                   int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  Plan pl;
+  BsaArgs ba;
+  int st = prepare_bsa(p, q, k, v, mask, mask_row_words, softmax_scale, out, lse, &pl, &ba);
+  if (st != STEM_OK) return st;
+  const bool expand = bsa_fp8_supported(p->dtype, p->head_dim, p->block);
+  const int64_t nv = expand ? v_elements(p, pl) : 0;
+  if (expand) {
+    if (!ws || ws_bytes < (size_t)nv * 2)
+      return fail(STEM_E_WORKSPACE, "workspace of %zu bytes, bsa_workspace_bytes = %zu", ws ? ws_bytes : (size_t)0,
+                  (size_t)nv * 2);
+    if ((uintptr_t)ws & 15) return fail(STEM_E_INVALID_ARG, "ws must be 16-byte aligned");
+  }
+  st = check_device();
+  if (st != STEM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (!expand)
+    return hip_status(launch_bsa(ba, p->dtype, p->head_dim, p->kv_paged != 0, mask != nullptr, s), "bsa launch");
+  hipError_t e = launch_expand_fp8(v, ws, nv, s);
+  if (e != hipSuccess) return hip_status(e, "V expansion launch");
+  ba.v = ws;
+  return hip_status(launch_bsa_fp8_vb16(ba, mask != nullptr, s), "bsa launch");
+}
+
 int bsa_prefill_inloop(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
                        int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream) {
   Plan pl;

@@ -129,5 +129,8 @@ hipError_t launch_bsa_bf16(const BsaArgs& a, bool masked, hipStream_t s);
 hipError_t launch_bsa_bf16_inloop(const BsaArgs& a, hipStream_t s);
 bool bsa_fp8_supported(int dtype, int head_dim, int block);
 hipError_t launch_bsa_fp8(const BsaArgs& a, bool masked, hipStream_t s);
+// fp8 attention reading V expanded to bf16 (a.v), and the expansion itself (n codes, a multiple of 16).
+hipError_t launch_bsa_fp8_vb16(const BsaArgs& a, bool masked, hipStream_t s);
+hipError_t launch_expand_fp8(const void* v_codes, void* v_bf16, int64_t n, hipStream_t s);
 
 }  // namespace stem

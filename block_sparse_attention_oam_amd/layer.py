@@ -36,6 +36,8 @@ class StemPrefill:
         out_dtype = torch.float32 if c.dtype == _abi.DTYPES["f32"] else torch.bfloat16
         self.out = torch.empty((self.tokens, c.hq, c.head_dim), dtype=out_dtype, device=device)
         self.lse = torch.empty((c.hq, self.tokens), dtype=torch.float32, device=device)
+        # attention workspace: V's bf16 expansion for fp8 problems, empty otherwise
+        self.bsa_ws = torch.empty(_abi.bsa_workspace_bytes(problem), dtype=torch.uint8, device=device)
 
     def pooled(self):
         """Views of the workspace: (qbar [hq][NB][d], kbar [hkv][NB][d], M [hkv][NB])."""
@@ -57,11 +59,19 @@ class StemPrefill:
         """Pooling, scoring and selection fused (no score tensor); fills mask and counts."""
         _abi.stem_score_select(self.p, q, k, v, beta, rho, mu, self.mask, self.counts, self.ws, stream)
 
-    def attend(self, q, k, v, mask="selected", lse=True, softmax_scale=0.0, stream=None, inloop=False):
-        """inloop=True runs the comparison variant that tests the mask inside the loop."""
+    def attend(self, q, k, v, mask="selected", lse=True, softmax_scale=0.0, stream=None, inloop=False,
+               expand_v=True):
+        """inloop=True runs the comparison variant that tests the mask inside the loop.  fp8 problems run
+        bsa_prefill_ws (V expanded to bf16 once per call) unless expand_v=False (bsa_prefill: V converted
+        per tile visit); the outputs are the same."""
         m = self.mask if isinstance(mask, str) and mask == "selected" else mask
-        fn = _abi.bsa_prefill_inloop if inloop else _abi.bsa_prefill
-        fn(self.p, q, k, v, m, self.out, self.lse if lse else None, softmax_scale, stream)
+        lse_t = self.lse if lse else None
+        if inloop:
+            _abi.bsa_prefill_inloop(self.p, q, k, v, m, self.out, lse_t, softmax_scale, stream)
+        elif expand_v and self.bsa_ws.numel() > 0:
+            _abi.bsa_prefill_ws(self.p, q, k, v, m, self.out, lse_t, softmax_scale, self.bsa_ws, stream)
+        else:
+            _abi.bsa_prefill(self.p, q, k, v, m, self.out, lse_t, softmax_scale, stream)
 
     def forward(self, q, k, v, beta=0.2, rho=(25, 100), mu=(7, 10), stream=None):
         self.score(q, k, v, beta, stream)

@@ -198,6 +198,24 @@ int stem_naive_score(const stem_problem* p, const void* q, const void* k, const 
 int bsa_prefill(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
                 int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* stream);
 
+/* Workspace bytes that bsa_prefill_ws needs: 2 bytes per V element (V's bf16 expansion) for fp8 problems
+ * of head_dim 128 and block 128 -- contiguous: tokens * hkv * head_dim elements; paged: num_pages *
+ * page_size * hkv * head_dim -- and 0 for every other problem (0 also on invalid input; see
+ * stem_last_error()). */
+size_t bsa_workspace_bytes(const stem_problem* p);
+
+/* bsa_prefill with a caller workspace; same arguments, outputs and limits otherwise.  For fp8 problems of
+ * head_dim 128 and block 128 it first expands V's e4m3 codes to bfloat16 into ws (exact: every e4m3 value
+ * is a bfloat16 value; v_scale still applies at the output), then runs the attention on that copy, which
+ * reaches LDS by direct loads instead of a conversion on every visit of a V tile; the outputs are bit for
+ * bit those of bsa_prefill.  Every other problem ignores ws and runs exactly as bsa_prefill.  ws: DEVICE,
+ * 16-byte aligned, ws_bytes >= bsa_workspace_bytes(p) (STEM_E_WORKSPACE otherwise), not overlapping the
+ * other buffers; it holds the bf16 V after the call.
+ * Source: "HPC-BSA：跳块零开销的秘密" (FP8 compute throughput) and "答案不在算法里" (W8A8-FP8). */
+int bsa_prefill_ws(const stem_problem* p, const void* q, const void* k, const void* v, const uint32_t* mask,
+                   int32_t mask_row_words, float softmax_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                   void* stream);
+
 /* Comparison variant of bsa_prefill with the skip decision inside the loop: instead of building each
  * row's list of selected blocks, it walks every causal block j <= i and tests j's mask bit at each step,
  * skipping the loads and the compute of unselected blocks but not the step.  Same arguments and same

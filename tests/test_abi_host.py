@@ -202,6 +202,8 @@ def test_invalid_problem_is_rejected_by_every_entry_point(kw, msg):
         lambda: stem.stem_tpd_topk(p, T(shape=(1, 1, 64)), (1, 4), (7, 10), T(shape=(1, 1, 2)), T(), stream=0),
         lambda: stem.bsa_prefill(p, T(), T(), T(), None, T(), stream=0),
         lambda: _abi.bsa_prefill_inloop(p, T(), T(), T(), T(shape=(8, 24, 1)), T(), stream=0),
+        lambda: stem.bsa_prefill_ws(p, T(), T(), T(), None, T(), ws=T(shape=(1 << 30,), elem=1), stream=0),
+        lambda: stem.bsa_workspace_bytes(p),
         lambda: stem.stem_score_select(p, T(), T(), T(), 0.2, (1, 4), (7, 10), T(shape=(1, 1, 2)), T(),
                                        T(shape=(1 << 30,), elem=1), stream=0),
     ]
@@ -363,6 +365,32 @@ def test_quantize_fp8_argument_errors():
     with pytest.raises(stem.StemError) as e:
         stem.stem_quantize_fp8(p, *a, stream=0)
     assert "aligned" in str(e.value)
+
+
+def test_bsa_workspace_bytes_and_argument_errors():
+    """bsa_prefill_ws needs 2 bytes per V element (the bf16 expansion) for fp8 at d = 128, B = 128 --
+    contiguous: tokens x hkv x d, paged: the whole pool -- and no workspace otherwise; a missing, short or
+    misaligned workspace is refused before anything is enqueued."""
+    T = _FakeTensor
+    f8 = dict(dtype="fp8", q_scale=T(), k_scale=T(), v_scale=T())
+    p = _prob(**f8)
+    need = 3000 * 2 * 128 * 2
+    assert stem.bsa_workspace_bytes(p) == need
+    pp = _prob(page_table=T(shape=(2, 64)), page_size=64, num_pages=70, **f8)
+    assert stem.bsa_workspace_bytes(pp) == 70 * 64 * 2 * 128 * 2
+    assert stem.bsa_workspace_bytes(_prob()) == 0
+    assert stem.bsa_workspace_bytes(_prob(dtype="f32")) == 0
+    assert stem.bsa_workspace_bytes(_prob(head_dim=64, **f8)) == 0
+    for ws, status, msg in ((None, _abi.STEM_E_WORKSPACE, "workspace"),
+                            (T(shape=(need - 1,), elem=1), _abi.STEM_E_WORKSPACE, "workspace"),
+                            (T(addr=0x10008, shape=(need,), elem=1), _abi.STEM_E_INVALID_ARG, "aligned")):
+        with pytest.raises(stem.StemError) as e:
+            stem.bsa_prefill_ws(p, T(), T(), T(), None, T(), ws=ws, stream=0)
+        assert e.value.status == status and msg in str(e.value), str(e.value)
+    # the other checks of bsa_prefill come first
+    with pytest.raises(stem.StemError) as e:
+        stem.bsa_prefill_ws(p, T(), T(), T(), T(shape=(8, 24, 0)), T(), ws=None, stream=0)
+    assert "mask_row_words" in str(e.value)
 
 
 def test_last_error_is_cleared_by_a_successful_call():

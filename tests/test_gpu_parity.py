@@ -522,8 +522,8 @@ def test_quantize_score_full_size_128k(dev):
 
 
 # ------------------------------------------------------------------------------------ fused scoring + selection
-def _fused_vs_two_stage(p, x, dev):
-    """Masks and counts from stem_score + stem_tpd_topk and from stem_score_select on the same inputs."""
+def _layer(p, x, dev):
+    """The problem descriptor, a StemPrefill and the device inputs of a synthetic workload."""
     import block_sparse_attention_oam_amd as stem
     from block_sparse_attention_oam_amd.layer import StemPrefill, upload
 
@@ -537,8 +537,12 @@ def _fused_vs_two_stage(p, x, dev):
     else:
         prob = stem.make_problem(p.cu_seqlens, p.hq, p.hkv, p.d, p.block, p.dtype, **kw)
         k, v = upload(x["k"]), upload(x["v"])
-    q = upload(x["q"])
-    L = StemPrefill(prob, dev)
+    return StemPrefill(prob, dev), upload(x["q"]), k, v
+
+
+def _fused_vs_two_stage(p, x, dev):
+    """Masks and counts from stem_score + stem_tpd_topk and from stem_score_select on the same inputs."""
+    L, q, k, v = _layer(p, x, dev)
     rho, mu = (p.rho_num, p.rho_den), (p.mu_num, p.mu_den)
     L.score(q, k, v, p.beta)
     L.select(rho, mu)
@@ -577,6 +581,58 @@ def test_fused_score_select_full_size(dev, name):
     x = synth.make_inputs(p, seed=0)
     L, m1, c1 = _fused_vs_two_stage(p, x, dev)
     assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
+
+
+# ------------------------------------------------------------------------------------ fp8: V expanded once
+def _expanded_vs_per_visit(p, x, dev, dense=False):
+    """Attention of an fp8 problem through bsa_prefill (V converted on every tile visit) and through
+    bsa_prefill_ws (V expanded to bf16 once), on the GPU's own selection (or dense)."""
+    L, q, k, v = _layer(p, x, dev)
+    L.score(q, k, v, p.beta)
+    L.select((p.rho_num, p.rho_den), (p.mu_num, p.mu_den))
+    mask = None if dense else "selected"
+    L.attend(q, k, v, mask, expand_v=False)
+    o1, l1 = L.out.clone(), L.lse.clone()
+    L.out.fill_(float("nan"))
+    L.lse.fill_(float("nan"))
+    L.bsa_ws.fill_(0xFF)
+    L.attend(q, k, v, mask, expand_v=True)
+    torch.cuda.synchronize()
+    return L, v, o1, l1
+
+
+FP8_CASES = [
+    dict(lens=(1000,), hq=8, hkv=2),                                 # two heads per workgroup
+    dict(lens=(700, 129), hq=3, hkv=1),                              # one head per workgroup
+    dict(lens=(300, 700), hq=4, hkv=2, paged=True, page_size=64),    # pages of 64 tokens
+    dict(lens=(129, 500), hq=8, hkv=2, paged=True, page_size=32),    # smaller pages
+    dict(lens=(1, 65, 128, 200), hq=2, hkv=1),                       # requests shorter than a sub-tile
+]
+
+
+@pytest.mark.parametrize("over", FP8_CASES, ids=[f"fp8-{i}" for i in range(len(FP8_CASES))])
+@pytest.mark.parametrize("dense", [False, True], ids=["selected", "dense"])
+def test_fp8_expanded_v_is_bit_identical_to_per_visit_conversion(dev, over, dense):
+    """The bf16 expansion equals torch's e4m3fn decode, and the attention on it reproduces bsa_prefill's
+    outputs and LSE bit for bit (both give the MFMAs the same bf16 V tile)."""
+    p = synth.make_problem("w8a8_128k_fp8", **over)
+    x = synth.make_inputs(p, seed=4)
+    L, v, o1, l1 = _expanded_vs_per_visit(p, x, dev, dense)
+    assert L.bsa_ws.numel() == 2 * v.numel()
+    dec = v.view(torch.float8_e4m3fn).to(torch.bfloat16).view(torch.int16).flatten()
+    assert torch.equal(L.bsa_ws.view(torch.int16), dec)
+    assert torch.equal(L.out.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(L.lse, l1)
+
+
+@pytest.mark.timeout(600)
+def test_fp8_expanded_v_full_size_128k(dev):
+    p = synth.make_problem("w8a8_128k_fp8")
+    _log("[fp8 expanded V] w8a8_128k_fp8")
+    x = synth.make_inputs(p, seed=0)
+    L, v, o1, l1 = _expanded_vs_per_visit(p, x, dev)
+    assert torch.equal(L.out.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(L.lse, l1)
 
 
 # ------------------------------------------------------------------------------------ naive comparison path
