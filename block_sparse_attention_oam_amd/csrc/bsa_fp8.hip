@@ -310,11 +310,16 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
 
   // Step u: K(u) (DMA) and V(u) (converted) are in LDS; K(u+1) and V(u+1) start loading into the other
   // buffers; V(u+1) is converted and stored after the compute, before the next barrier.
+  // With V expanded and two heads over a list of at most 3/4 of the row's causal blocks, the first head's
+  // waves issue their share of the next sub-tile's loads at the end of the step (the buffers are free
+  // from the barrier on), so the second head's waves, which each SIMD serves last, do not queue behind
+  // them in the memory pipe (as in the bf16 kernel; 1% faster on the W8A8 128K layer).
+  const bool at_end = VB16 && HEADS == 2 && MASKED && hsel == 0 && 4 * nsel <= 3 * (i + 1);
   auto step = [&](int u, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const bool more = u + 1 < nsub;
-    if (more) {
+    if (more && !at_end) {
       if constexpr (VB16) issue_v16(u + 1, vnext);
       else load_v(u + 1);
       issue_k(u + 1, knext);
@@ -433,6 +438,11 @@ __global__ __launch_bounds__(256 * HEADS, 2 / HEADS) void bsa_fp8_kernel(BsaArgs
     }
     if constexpr (!VB16)
       if (more) store_v(vnext);
+    if constexpr (VB16)
+      if (more && at_end) {
+        issue_v16(u + 1, vnext);
+        issue_k(u + 1, knext);
+      }
   };
 
   if (nsub > 0) {

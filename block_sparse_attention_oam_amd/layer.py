@@ -73,8 +73,13 @@ class StemPrefill:
         else:
             _abi.bsa_prefill(self.p, q, k, v, m, self.out, lse_t, softmax_scale, stream)
 
-    def forward(self, q, k, v, beta=0.2, rho=(25, 100), mu=(7, 10), stream=None):
-        self.score(q, k, v, beta, stream)
-        self.select(rho, mu, stream)
+    def forward(self, q, k, v, beta=0.2, rho=(25, 100), mu=(7, 10), stream=None, fused=True):
+        """Score, select, attend.  fused: scoring and selection in one kernel (no score tensor; the same
+        masks) where the library supports it (up to 2048 blocks per request), else the two stages."""
+        if fused and self.max_n <= 2048:
+            self.score_select(q, k, v, beta, rho, mu, stream)
+        else:
+            self.score(q, k, v, beta, stream)
+            self.select(rho, mu, stream)
         self.attend(q, k, v, "selected", True, 0.0, stream)
         return self.out
