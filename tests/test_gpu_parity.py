@@ -583,6 +583,32 @@ def test_fused_score_select_full_size(dev, name):
     assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
 
 
+def test_scoring_beyond_2048_blocks_and_batch_independence(dev):
+    """stem_score has no 2048-block limit (only the fused selection and masked attention do): a batch whose
+    longest request has 2100 blocks, every score against the oracle; and its second request, scored again
+    alone, gives the same scores bit for bit (a request's scores do not depend on its batch)."""
+    p = synth.make_problem("llama_32k_bf16", lens=(2100 * 64, 1000 * 64 - 7), hq=2, hkv=1, d=64, block=64)
+    x = synth.make_inputs(p, seed=3)
+    L, q, k, v = _layer(p, x, dev)
+    L.scores.fill_(float("nan"))
+    L.score(q, k, v, p.beta)
+    torch.cuda.synchronize()
+    qb, kb, M = L.pooled()
+    g = {"qbar": qb.cpu().numpy(), "kbar": kb.cpu().numpy(), "M": M.cpu().numpy(), "scores": L.scores.cpu().numpy()}
+    _log("[scores > 2048 blocks] oracle")
+    _check_stage1(p, g, sc.oracle_stage1(p, x))
+    t0 = p.lens[0]
+    p2 = synth.make_problem("llama_32k_bf16", lens=(p.lens[1],), hq=2, hkv=1, d=64, block=64)
+    x2 = dict(x, q=x["q"][t0:], k=x["k"][t0:], v=x["v"][t0:])
+    L2, q2, k2, v2 = _layer(p2, x2, dev)
+    L2.scores.fill_(float("nan"))
+    L2.score(q2, k2, v2, p2.beta)
+    torch.cuda.synchronize()
+    n2, cb = p2.nblocks(0), p.cu_blocks[1]
+    tri = torch.tril(torch.ones(n2, n2, dtype=torch.bool, device=dev))
+    assert torch.equal(L2.scores[:, :n2, :n2][:, tri], L.scores[:, cb:cb + n2, :n2][:, tri])
+
+
 # ------------------------------------------------------------------------------------ fp8: V expanded once
 def _expanded_vs_per_visit(p, x, dev, dense=False):
     """Attention of an fp8 problem through bsa_prefill (V converted on every tile visit) and through
