@@ -472,7 +472,7 @@ int stem_score_select(const stem_problem* p, const void* q, const void* k, const
   if (e != hipSuccess) return hip_status(e, "pool launch");
   size_t oq, okk, om, need;
   layout(pl, &oq, &okk, &om, &need);
-  ScoreTopkArgs a;
+  ScoreTopkArgs a{};
   a.qbar = (const float*)((char*)ws + oq);
   a.kbar = (const float*)((char*)ws + okk);
   a.M = (const float*)((char*)ws + om);
