@@ -661,6 +661,20 @@ def test_fp8_expanded_v_full_size_128k(dev):
     assert torch.equal(L.lse, l1)
 
 
+@pytest.mark.parametrize("hq,hkv", [(3, 3), (2, 1)], ids=["one-head-per-workgroup", "two-heads-per-workgroup"])
+def test_fused_score_select_beyond_1024_blocks(dev, hq, hkv):
+    """Rows of 1025-2048 blocks take the fused kernel's widest register layout (32 slots per lane), with one
+    query head per workgroup (odd group size) or two: masks and counts equal to the two-stage path's, and
+    every budget and selection against the oracle."""
+    p = synth.make_problem("llama_32k_bf16", lens=(1300 * 64 - 5,), hq=hq, hkv=hkv, d=64, block=64)
+    x = synth.make_inputs(p, seed=12)
+    L, m1, c1 = _fused_vs_two_stage(p, x, dev)
+    assert torch.equal(L.mask, m1) and torch.equal(L.counts, c1)
+    ref1 = sc.oracle_stage1(p, x)
+    sc.check_selection(p, [s for *_, s in ref1], sc.oracle_budgets(p), L.mask.cpu().numpy().view(np.uint32),
+                       L.counts.cpu().numpy())
+
+
 # ------------------------------------------------------------------------------------ naive comparison path
 def _naive_gpu(p, x, dev, samples):
     import block_sparse_attention_oam_amd as stem
