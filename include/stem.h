@@ -12,6 +12,14 @@
  *                  blocks (skipped blocks behave as -inf scores); or dense causal attention when no mask
  *                  is given.  Source: same page, section "HPC-BSA：跳块零开销的秘密" (including its
  *                  paged-KV-cache paragraph).
+ * Variants of the same stages, declared below with their own notes:
+ *   stem_score_select     stem_score and stem_tpd_topk in one pass, without the score tensor.
+ *   stem_quantize_score   W8A8: bf16 Q/K/V to per-head-scaled e4m3 codes, pooled in the same pass, scored.
+ *   stem_quantize_fp8     the quantisation alone (the unfused baseline of stem_quantize_score).
+ *   stem_score_noalloc    stem_score with its pooled tensors in a static per-device scratch.
+ *   bsa_prefill_ws        bsa_prefill with a workspace (fp8: V expanded to bf16 once per call).
+ *   bsa_prefill_inloop    bsa_prefill with the skip test inside the loop (a comparison path).
+ *   stem_naive_score      token-level softmax scoring of sampled queries (a comparison path).
  *
  * Conventions (all entry points):
  *   - Plain C types only.  `stream` is a hipStream_t passed as void* (NULL = the null stream).
