@@ -458,7 +458,7 @@ def main():
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the library has no multi-GPU path; "
               f"each GPU's share would be this single-GPU kernel on its KV-head group.", file=sys.stderr)
         sys.exit(2)
 
